@@ -1,0 +1,226 @@
+"""Throughput of the INSTANT low-rank backward on one MI355X.
+
+Workload: BERT-base attention-projection-shaped linear y = x w^T, bf16 I/O with
+float32 accumulation, B=32 sequences of L=512 tokens, Cx=Cy=768, eps=0.95, p=2,
+statistics over N_cal=16 batches, recalibration every N_t=100 steps (shapes of the
+BERT layers the INSTANT notes evaluate; synthetic token-low-rank data, see
+workloads/).
+
+One step is one training step's share of the method on one batch, on the notes'
+schedule (section 整体框架): every step compresses x (x_hat = P x) and runs the
+low-rank backward (g_w, g_x); the first N_cal steps of every N_t-step window also
+accumulate the statistics, and the last of them finalizes (eigen-decomposition,
+truncation, new P and Q). So every kernel of the path runs inside the timed region,
+with the calibration amortised exactly as the schedule amortises it.
+
+Prints one JSON line; `value` is tokens/s = steps * B * L / wall time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="bert_attn")
+    ap.add_argument("--batches", type=int, default=16, help="distinct resident batches cycled through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=8, help="samples of a batch the oracle times")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the multi-GPU data-parallel path is a design, not built "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rank_compressed_backprop_amd as rcb
+    import workloads as W
+
+    wl = W.get_workload(args.workload)
+    ly = wl.layer(0)
+    B, L, Cx, Cy = wl.B, wl.L, ly.Cx, ly.Cy
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+    def up(a):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    # resident synthetic batches (distinct, so the 256 MB last-level cache cannot hold a step's data)
+    nb = max(args.batches, wl.n_cal)
+    xs, gys = [], []
+    for t in range(nb):
+        d = W.make_layer_batch(wl, 0, t)
+        xs.append(up(d["x"]))
+        gys.append(up(d["gy"]))
+    w = up(W.to_io(W.make_w(wl, 0), wl.dtype))
+    del d
+
+    R_max = 64
+    lay = rcb.InstantLayer(rcb.make_config(L, Cx, Cy, B, R_max=R_max, p=wl.p, N_t=wl.n_t, eps=wl.eps,
+                                           dtype=wl.dtype, comp="paper"), device=dev)
+    xhat = torch.empty((B, R_max, Cx), dtype=tdt, device=dev)
+    gw = torch.empty((Cy, Cx), dtype=tdt, device=dev)
+    gx = torch.empty((B, L, Cx), dtype=tdt, device=dev)
+
+    # initial calibration (set-up, untimed)
+    for t in range(wl.n_cal):
+        s = lay.calibrate(xs[t], gys[t], B, finalize=(t == wl.n_cal - 1))
+        assert s == rcb.INSTANT_OK, rcb.instant_status_str(s)
+
+    def step(i):
+        t = i % nb
+        ph = i % wl.n_t
+        lay.compress_fwd(xs[t], B, xhat)
+        lay.backward(xhat, gys[t], w, B, gw, gx)
+        if ph < wl.n_cal:
+            s = lay.calibrate(xs[t], gys[t], B, finalize=(ph == wl.n_cal - 1))
+            if s != rcb.INSTANT_OK:
+                raise RuntimeError("calibration failed: " + rcb.instant_status_str(s))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, args.warmup + args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    _, info = lay.query()
+    Rx, Ry = info.Rx, info.Ry
+
+    # ---- per-part timing with HIP events on the launch stream (outside the timed region)
+    st = torch.cuda.current_stream()
+
+    def ev_time(fn, reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn(0)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for r in range(reps):
+            fn(r)
+        e1.record(st)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3  # seconds
+
+    reps = 200
+    t_fwd = ev_time(lambda r: lay.compress_fwd(xs[r % nb], B, xhat), reps)
+    t_bwd = ev_time(lambda r: lay.backward(xhat, gys[r % nb], w, B, gw, gx), reps)
+    t_acc = ev_time(lambda r: lay.calibrate(xs[r % nb], gys[r % nb], B, finalize=False), 50)
+    # one full finalize (eigen-decomposition of both statistics, truncation, publish)
+    torch.cuda.synchronize()
+    tf0 = time.perf_counter()
+    s = lay.calibrate(None, None, 0, finalize=True)
+    torch.cuda.synchronize()
+    t_fin = time.perf_counter() - tf0
+    _, info2 = lay.query()
+
+    es = 2 if wl.dtype == "bf16" else 4
+    bytes_fwd = es * (B * L * Cx + B * Rx * Cx)
+    bytes_bwd = es * (B * L * Cy + B * Rx * Cx + 2 * Cx * Cy + B * L * Cx)
+    flops_bwd = B * (2 * (Rx + Ry) * L * Cy + 2 * (Rx + Ry) * Cx * Cy + 2 * Ry * L * Cx)
+    gbs_fwd = bytes_fwd / t_fwd / 1e9
+
+    ms_per_step = wall / args.steps * 1e3
+    tokens = args.steps * B * L
+    value = tokens / wall
+
+    out = {
+        "metric": "low-rank backward tokens/s + achieved HBM GB/s (% peak), BERT-base linear",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"BERT-base attention projection linear, B={B} L={L} Cx={Cx} Cy={Cy}, "
+                               f"eps={wl.eps} p={wl.p} N_cal={wl.n_cal} N_t={wl.n_t}",
+                   "global_batch": B, "seq_len": L, "parallelism": "single GPU",
+                   "step": "compress + low-rank backward every step; statistics on the first N_cal steps of "
+                           "each N_t window; eigen-decomposition + truncation once per window",
+                   "Rx": Rx, "Ry": Ry, "kx": info.kx, "ky": info.ky},
+        "parts": {
+            "compress_fwd_us": t_fwd * 1e6, "compress_fwd_GBs": gbs_fwd,
+            "backward_us": t_bwd * 1e6, "backward_GBs": bytes_bwd / t_bwd / 1e9,
+            "backward_pct_hbm_peak": 100.0 * bytes_bwd / t_bwd / 1e9 / HBM_PEAK_GBS,
+            "backward_tokens_per_s": B * L / t_bwd, "backward_TFLOPs": flops_bwd / t_bwd / 1e12,
+            "statistics_per_batch_us": t_acc * 1e6,
+            "finalize_ms": t_fin * 1e3, "jacobi_sweeps": [info2.sweeps_x, info2.sweeps_g],
+            "finalize_status": rcb.instant_status_str(s),
+        },
+        "roofline": {"kernel": "proj (forward compression x_hat = P x)", "bound": "hbm",
+                     "achieved": gbs_fwd, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs_fwd / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": bytes_fwd},
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, nsample):
+    """The CPU oracle (float64 numpy) timed on a bounded sample of the same step."""
+    import numpy as np
+
+    import oracle as O
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    ly = wl.layer(0)
+    d = W.make_layer_batch(wl, 0, 0, with_w=True)
+    xs, gys, w = d["x64"][:nsample], d["gy64"][:nsample], d["w64"]
+    cal = O.calibrate([d["x64"]], [d["gy64"]], wl.eps, wl.p, O.COMP_PAPER)
+    P, Q = cal["x"]["P"], cal["g"]["P"]
+    t0 = time.perf_counter()
+    xh = O.compress(P, xs)
+    O.backward(P, Q, xh, gys, w)
+    t_cb = (time.perf_counter() - t0) / nsample            # per sample
+    t0 = time.perf_counter()
+    acc = O.Accumulator(wl.L)
+    acc.add(xs)
+    acc.add(gys)
+    t_acc = (time.perf_counter() - t0) / nsample            # per sample, both tensors
+    t0 = time.perf_counter()
+    O.calibrate_side(cal["C_X"], wl.eps, wl.p, O.COMP_PAPER, wl.L)
+    O.calibrate_side(cal["C_G"], wl.eps, wl.p, O.COMP_PAPER, wl.L)
+    t_fin = time.perf_counter() - t0                        # per finalize
+    per_step = wl.B * t_cb + (wl.n_cal / wl.n_t) * wl.B * t_acc + t_fin / wl.n_t
+    return {"value": wl.B * wl.L / per_step, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{nsample} of {wl.B} samples of one batch for compress+backward and the statistics, "
+                      f"one full finalize (eigh of both {wl.L}x{wl.L} statistics); per-step time = "
+                      f"B*t_sample(compress+backward) + (N_cal/N_t)*B*t_sample(statistics) + t_finalize/N_t",
+            "seconds_per_step": per_step}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+/*
+ * instant.h - C ABI of the INSTANT low-rank backward for a linear layer y = x . w^T
+ *
+ * Method: the notes "INSTANT: Compressing Gradients and Activations for
+ * Resource-Efficient Training" (papernotes.org, ICLR 2026). Section keys used below:
+ *   [Framework] 整体框架   forward unchanged; x_hat = P x is stored instead of x;
+ *                           P and Q are refreshed every N_t steps
+ *   [KD1]       关键设计 1 per-tensor token autocorrelations C_X = E[x x^T], C_G = E[g_y g_y^T],
+ *                           batch not folded into the decomposition; only the statistics are kept
+ *   [KD2]       关键设计 2 energy threshold k, p oversampled bases, the compensation in the
+ *                           Q equation; P in R^{Rx x L}, Q in R^{Ry x L}
+ *   [KD3]       关键设计 3 reordered products g_w ~ (g_y^T P^T)(P x),
+ *                           g_x ~ Q^T ((Q g_y) w)
+ *
+ * Shapes and layouts (all row-major, channels contiguous):
+ *   x     [B, L, Cx]      activations of the linear layer's input
+ *   gy    [B, L, Cy]      gradient of the layer output
+ *   w     [Cy, Cx]        weight (y = x . w^T)
+ *   xhat  [B, Rx, Cx]     compressed activation (rows packed with the current Rx)
+ *   gw    [Cy, Cx]        weight gradient (overwritten)
+ *   gx    [B, L, Cx]      input gradient (overwritten)
+ *   P     [Rx, L], Q [Ry, L]  projections, float32 masters
+ *
+ * Conventions
+ *   - Every pointer named as "device" is owned by the caller. The library never
+ *     allocates device memory: all device state lives in the caller's workspace
+ *     (instant_workspace_bytes). The host handle and one small pinned host block
+ *     are the library's own.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*; NULL is
+ *     the default stream) except instant_query, which waits for the last
+ *     calibration result, and the first compress/backward call after a finalize,
+ *     which waits once for the new ranks (Rx, Ry size the launches).
+ *   - Host-detectable errors return at once with no side effect.
+ *     Device-detected calibration failures are latched; the previous projections
+ *     stay active and instant_query reports the failure.
+ *   - The I/O dtype (x, gy, w, xhat, gw, gx) is fixed per handle: float32 or
+ *     bfloat16. Accumulation is float32; statistics are summed in float64 across
+ *     batches.
+ *   - Cx and Cy must be multiples of 8; L >= 1; 1 <= R_max <= 64 and R_max <= L.
+ *   - A handle is used from one stream at a time; calls are not re-entrant.
+ */
+#ifndef INSTANT_H_
+#define INSTANT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  INSTANT_OK = 0,
+  INSTANT_E_ARG = 1,        /* null pointer, bad enum, non-positive size */
+  INSTANT_E_SHAPE = 2,      /* sizes outside what the handle was created for */
+  INSTANT_E_STATE = 3,      /* compress/backward before any projection exists */
+  INSTANT_E_RANK = 4,       /* k + p exceeds R_max ([KD2]) */
+  INSTANT_E_ENERGY = 5,     /* statistics with zero energy ([KD2]: E = 0) */
+  INSTANT_E_NONFINITE = 6,  /* NaN or Inf in the statistics */
+  INSTANT_E_NOCONV = 7,     /* eigensolver did not converge within max_sweeps */
+  INSTANT_E_HIP = 8         /* a HIP runtime call or kernel launch failed */
+} instant_status;
+
+typedef enum { INSTANT_FP32 = 0, INSTANT_BF16 = 1 } instant_dtype;
+
+/* Energy compensation applied to the kept bases ([KD2], the Q equation):
+ *   PAPER: c = (sum_{i<=R} sigma_i^2)^(-1/2), as printed
+ *   NONE : c = 1 (orthonormal rows)
+ *   RATIO: c = (E / sum_{i<=R} sigma_i^2)^(1/2), E = sum_i sigma_i^2
+ * with P = c * U_R^T. */
+typedef enum { INSTANT_COMP_PAPER = 0, INSTANT_COMP_NONE = 1, INSTANT_COMP_RATIO = 2 } instant_comp;
+
+typedef struct {
+  int32_t L;          /* tokens per sample */
+  int32_t Cx, Cy;     /* input / output channels */
+  int32_t B_max;      /* largest batch any call will pass */
+  int32_t R_max;      /* largest Rx or Ry the handle accepts (<= 64, <= L) */
+  int32_t p;          /* oversampled bases added to k ([KD2]) */
+  int32_t N_t;        /* recalibration period, kept for bookkeeping ([Framework]) */
+  float eps;          /* energy threshold, 0 < eps <= 1 ([KD2]) */
+  int32_t dtype;      /* instant_dtype of x, gy, w, xhat, gw, gx */
+  int32_t comp;       /* instant_comp */
+  int32_t max_sweeps; /* Jacobi sweep limit (e.g. 30) */
+} instant_config;
+
+typedef struct {
+  int32_t kx, ky;           /* truncation indices ([KD2]) */
+  int32_t Rx, Ry;           /* ranks in use = min(k + p, L) */
+  int32_t sweeps_x, sweeps_g;
+  int32_t status;           /* instant_status of the last finalize */
+  float cP, cQ;             /* compensation scalars */
+  double kept_x, kept_g;    /* sum_{i<=R} sigma_i^2 / E */
+  int64_t n_samples_x, n_samples_g; /* samples in the statistics of the last finalize */
+  uint32_t generation;      /* bumped each time new projections become active */
+} instant_info;
+
+typedef struct instant_layer instant_layer;
+
+/* Bytes of device workspace the handle needs for `cfg` (0 if cfg is invalid). */
+size_t instant_workspace_bytes(const instant_config* cfg);
+
+/* Create a handle over the caller's device workspace (instant_workspace_bytes(cfg)
+ * bytes, 256-byte aligned). Clears the statistics on `stream`. The workspace must
+ * outlive the handle. Errors: E_ARG (null, invalid cfg), E_HIP. */
+instant_status instant_create(instant_layer** h, const instant_config* cfg, void* workspace, void* stream);
+
+/* Release the host handle (not the workspace). */
+instant_status instant_destroy(instant_layer* h);
+
+/* [KD1] calibration statistics. Adds sum_b x_b x_b^T to the C_X sum (x may be NULL)
+ * and sum_b gy_b gy_b^T to the C_G sum (gy may be NULL); B <= B_max.
+ * finalize != 0 then turns both sums into means over the samples seen, takes the
+ * eigen-decomposition of each, truncates at the energy threshold with p extra
+ * bases, applies the compensation ([KD2]), publishes the new P and Q and clears
+ * the sums. A finalize needs samples on both sides. */
+instant_status instant_calibrate(instant_layer* h, const void* x, const void* gy, int32_t B,
+                                 int32_t finalize, void* stream);
+
+/* [Framework] forward compression: xhat_b = P x_b for b < B. xhat holds B*Rx*Cx
+ * elements (allocate with R_max to be safe). Errors: E_ARG, E_SHAPE, E_STATE, E_HIP. */
+instant_status instant_compress_fwd(instant_layer* h, const void* x, int32_t B, void* xhat, void* stream);
+
+/* [KD3] low-rank backward:
+ *   gw     = sum_b (P gy_b)^T xhat_b                        [Cy, Cx]
+ *   gx_b   = Q^T ((Q gy_b) w)                               [L, Cx]
+ * gy is read once for both projections. xhat must come from instant_compress_fwd
+ * under the same projections. Errors: E_ARG, E_SHAPE, E_STATE, E_HIP. */
+instant_status instant_backward(instant_layer* h, const void* xhat, const void* gy, const void* w,
+                                int32_t B, void* gw, void* gx, void* stream);
+
+/* Wait for the last finalize (if any is pending) and report its result. Returns
+ * the latched device status of that finalize (INSTANT_OK if none failed). */
+instant_status instant_query(instant_layer* h, instant_info* out);
+
+/* Install projections directly (float32 device arrays P [Rx, L], Q [Ry, L]) with
+ * no calibration; for checkpoint resume and for testing the hot path alone.
+ * 1 <= Rx, Ry <= R_max. The data are copied into the workspace on `stream`. */
+instant_status instant_set_projections(instant_layer* h, const float* P, int32_t Rx, const float* Q,
+                                       int32_t Ry, void* stream);
+
+/* Copy out the active projections and the last spectra (any pointer may be NULL):
+ * P [Rx, L], Q [Ry, L] float32; sigma_x, sigma_g [L] float32 in descending order
+ * (the singular values of C_X and C_G from the last finalize). Device pointers. */
+instant_status instant_get_projections(instant_layer* h, float* P, float* Q, float* sigma_x,
+                                       float* sigma_g, void* stream);
+
+/* Copy out the current statistic means C_X, C_G [L, L] float64 (device pointers,
+ * either may be NULL), i.e. the running sums divided by the samples seen so far. */
+instant_status instant_get_statistics(instant_layer* h, double* C_X, double* C_G, void* stream);
+
+/* Name of a status code. */
+const char* instant_status_str(instant_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INSTANT_H_ */

@@ -1,0 +1,347 @@
+// Host runtime of the INSTANT C ABI (include/instant.h): argument checks, workspace
+// layout, stream-ordered launches of the kernels, calibration bookkeeping.
+//
+// Method: notes "INSTANT: Compressing Gradients and Activations for Resource-Efficient
+// Training" — 整体框架 (forward keeps x_hat = P x; P, Q refreshed every N_t steps),
+// 关键设计 1 (statistics C_X, C_G), 关键设计 2 (truncation, oversampling, compensation),
+// 关键设计 3 (reordered low-rank products).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+
+#include "instant.h"
+#include "launch.hpp"
+
+#define INSTANT_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using namespace instant;
+
+constexpr int MAX_L = 4096;
+constexpr int MAX_R = 64;
+constexpr int LD_QT = 64;
+constexpr int SYRK_TARGET_BLOCKS = 1024;
+constexpr int SYRK_MAX_SPLIT = 64;
+
+inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+inline int syrk_split_cap(int L) {
+  const int nt = syrk_tiles(L);
+  return std::max(1, std::min(SYRK_MAX_SPLIT, (SYRK_TARGET_BLOCKS + nt - 1) / nt));
+}
+
+bool config_ok(const instant_config* c) {
+  if (!c) return false;
+  if (c->L < 1 || c->L > MAX_L) return false;
+  if (c->Cx < 8 || c->Cy < 8 || (c->Cx % 8) || (c->Cy % 8)) return false;
+  if (c->B_max < 1) return false;
+  if (c->R_max < 1 || c->R_max > MAX_R || c->R_max > c->L) return false;
+  if (c->p < 0 || c->N_t < 0) return false;
+  if (!(c->eps > 0.0f && c->eps <= 1.0f)) return false;
+  if (c->dtype != INSTANT_FP32 && c->dtype != INSTANT_BF16) return false;
+  if (c->comp < INSTANT_COMP_PAPER || c->comp > INSTANT_COMP_RATIO) return false;
+  if (c->max_sweeps < 1) return false;
+  return true;
+}
+
+struct Layout {
+  size_t SX, SG, part, eig, sig_x, sig_g, info, rank, P32[2], Q32[2], PQ[2], Qt[2], Pgy, Qgy, gxh, total;
+  int ldL;
+};
+
+Layout layout_of(const instant_config* c) {
+  Layout l;
+  const size_t esz = c->dtype == INSTANT_BF16 ? 2 : 4;
+  const size_t L = c->L;
+  l.ldL = (c->L + 31) / 32 * 32;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  l.SX = take(L * L * sizeof(double));
+  l.SG = take(L * L * sizeof(double));
+  l.part = take((size_t)syrk_split_cap(c->L) * syrk_tiles(c->L) * 64 * 64 * sizeof(float));
+  l.eig = take(eig_workspace_bytes(c->L));
+  l.sig_x = take(L * sizeof(float));
+  l.sig_g = take(L * sizeof(float));
+  l.info = take(2 * INFO_WORDS * sizeof(int));
+  l.rank = take(2 * sizeof(int));
+  for (int b = 0; b < 2; ++b) {
+    l.P32[b] = take((size_t)c->R_max * L * sizeof(float));
+    l.Q32[b] = take((size_t)c->R_max * L * sizeof(float));
+    l.PQ[b] = take((size_t)2 * c->R_max * l.ldL * esz);
+    l.Qt[b] = take(L * LD_QT * esz);
+  }
+  l.Pgy = take((size_t)c->B_max * c->R_max * c->Cy * esz);
+  l.Qgy = take((size_t)c->B_max * c->R_max * c->Cy * esz);
+  l.gxh = take((size_t)c->B_max * c->R_max * c->Cx * esz);
+  l.total = off;
+  return l;
+}
+
+}  // namespace
+
+struct instant_layer {
+  instant_config cfg;
+  bool bf16;
+  char* ws;
+  Layout lay;
+  int active;  // projection buffer in use, -1 before the first one
+  int Rx, Ry;
+  int64_t nx, ng;
+  instant_info info;
+  instant_status last;
+
+  double* SX() const { return (double*)(ws + lay.SX); }
+  double* SG() const { return (double*)(ws + lay.SG); }
+  float* part() const { return (float*)(ws + lay.part); }
+  int* info_dev() const { return (int*)(ws + lay.info); }
+  int* rank_dev() const { return (int*)(ws + lay.rank); }
+  float* P32(int b) const { return (float*)(ws + lay.P32[b]); }
+  float* Q32(int b) const { return (float*)(ws + lay.Q32[b]); }
+  void* PQ(int b) const { return ws + lay.PQ[b]; }
+  void* Qt(int b) const { return ws + lay.Qt[b]; }
+};
+
+namespace {
+
+inline hipStream_t S(void* stream) { return (hipStream_t)stream; }
+inline instant_status hip_ok(hipError_t e) { return e == hipSuccess ? INSTANT_OK : INSTANT_E_HIP; }
+
+instant_status accumulate(instant_layer* h, const void* t, int B, int C, double* Sacc, hipStream_t st) {
+  const int steps = (C + (h->bf16 ? 32 : 16) - 1) / (h->bf16 ? 32 : 16);
+  const long total = (long)B * steps;
+  int nsplit = (int)std::min<long>(syrk_split_cap(h->cfg.L), std::max<long>(1, total / 4));
+  hipError_t e = launch_syrk(h->bf16, t, B, h->cfg.L, C, nsplit, h->part(), st);
+  if (e != hipSuccess) return INSTANT_E_HIP;
+  return hip_ok(launch_syrk_reduce(h->part(), nsplit, h->cfg.L, Sacc, st));
+}
+
+}  // namespace
+
+INSTANT_API size_t instant_workspace_bytes(const instant_config* cfg) {
+  if (!config_ok(cfg)) return 0;
+  return layout_of(cfg).total;
+}
+
+INSTANT_API instant_status instant_create(instant_layer** h, const instant_config* cfg, void* workspace,
+                                          void* stream) {
+  if (!h || !config_ok(cfg) || !workspace) return INSTANT_E_ARG;
+  if (((uintptr_t)workspace) % 256) return INSTANT_E_ARG;
+  instant_layer* L = new (std::nothrow) instant_layer();
+  if (!L) return INSTANT_E_ARG;
+  L->cfg = *cfg;
+  L->bf16 = cfg->dtype == INSTANT_BF16;
+  L->ws = (char*)workspace;
+  L->lay = layout_of(cfg);
+  L->active = -1;
+  L->Rx = L->Ry = 0;
+  L->nx = L->ng = 0;
+  std::memset(&L->info, 0, sizeof(L->info));
+  L->last = INSTANT_OK;
+  // statistics start at zero; the rest of the workspace is written before it is read
+  hipError_t e = launch_zero(L->SX(), (size_t)cfg->L * cfg->L * sizeof(double), S(stream));
+  if (e == hipSuccess) e = launch_zero(L->SG(), (size_t)cfg->L * cfg->L * sizeof(double), S(stream));
+  if (e != hipSuccess) {
+    delete L;
+    return INSTANT_E_HIP;
+  }
+  *h = L;
+  return INSTANT_OK;
+}
+
+INSTANT_API instant_status instant_destroy(instant_layer* h) {
+  if (!h) return INSTANT_E_ARG;
+  delete h;
+  return INSTANT_OK;
+}
+
+INSTANT_API instant_status instant_calibrate(instant_layer* h, const void* x, const void* gy, int32_t B,
+                                             int32_t finalize, void* stream) {
+  if (!h) return INSTANT_E_ARG;
+  if (B < 0 || B > h->cfg.B_max) return (B < 0) ? INSTANT_E_ARG : INSTANT_E_SHAPE;
+  if ((x || gy) && B < 1) return INSTANT_E_ARG;
+  if (!x && !gy && !finalize) return INSTANT_E_ARG;
+  hipStream_t st = S(stream);
+  if (finalize) {
+    const int64_t nx = h->nx + (x ? B : 0), ng = h->ng + (gy ? B : 0);
+    if (nx == 0 || ng == 0) return INSTANT_E_STATE;
+  }
+  instant_status s;
+  if (x) {
+    if ((s = accumulate(h, x, B, h->cfg.Cx, h->SX(), st)) != INSTANT_OK) return s;
+    h->nx += B;
+  }
+  if (gy) {
+    if ((s = accumulate(h, gy, B, h->cfg.Cy, h->SG(), st)) != INSTANT_OK) return s;
+    h->ng += B;
+  }
+  if (!finalize) return INSTANT_OK;
+
+  const int t = (h->active == 0) ? 1 : 0;
+  EigOut out;
+  out.eps = h->cfg.eps;
+  out.p = h->cfg.p;
+  out.comp = h->cfg.comp;
+  out.R_max = h->cfg.R_max;
+  out.P32 = h->P32(t);
+  out.Q32 = h->Q32(t);
+  out.sigma_x = (float*)(h->ws + h->lay.sig_x);
+  out.sigma_g = (float*)(h->ws + h->lay.sig_g);
+  out.info_x = h->info_dev();
+  out.info_g = h->info_dev() + INFO_WORDS;
+  int flags[10];
+  hipError_t e = run_eig(h->SX(), h->SG(), 1.0 / (double)h->nx, 1.0 / (double)h->ng, h->cfg.L, h->cfg.max_sweeps,
+                         h->ws + h->lay.eig, out, flags, st);
+  if (e != hipSuccess) return INSTANT_E_HIP;
+  int info[2 * INFO_WORDS];
+  e = hipMemcpyAsync(info, h->info_dev(), sizeof(info), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return INSTANT_E_HIP;
+  const int* ix = info;
+  const int* ig = info + INFO_WORDS;
+  instant_status status = (instant_status)(ix[0] != 0 ? ix[0] : ig[0]);
+
+  instant_info& I = h->info;
+  I.kx = ix[1];
+  I.ky = ig[1];
+  I.sweeps_x = flags[4];
+  I.sweeps_g = flags[5];
+  I.status = status;
+  float c;
+  std::memcpy(&c, &ix[3], 4);
+  I.cP = c;
+  std::memcpy(&c, &ig[3], 4);
+  I.cQ = c;
+  std::memcpy(&I.kept_x, &ix[4], 8);
+  std::memcpy(&I.kept_g, &ig[4], 8);
+  I.n_samples_x = h->nx;
+  I.n_samples_g = h->ng;
+  if (status == INSTANT_OK) {
+    e = launch_build_io(h->bf16, h->P32(t), h->Q32(t), h->info_dev() + 2, h->info_dev() + INFO_WORDS + 2, h->cfg.L,
+                        h->lay.ldL, h->cfg.R_max, h->PQ(t), h->Qt(t), LD_QT, st);
+    if (e != hipSuccess) return INSTANT_E_HIP;
+    h->active = t;
+    h->Rx = ix[2];
+    h->Ry = ig[2];
+    I.Rx = h->Rx;
+    I.Ry = h->Ry;
+    I.generation += 1;
+  }
+  h->last = status;
+  // the statistics window is consumed whatever the outcome
+  h->nx = h->ng = 0;
+  e = launch_zero(h->SX(), (size_t)h->cfg.L * h->cfg.L * sizeof(double), st);
+  if (e == hipSuccess) e = launch_zero(h->SG(), (size_t)h->cfg.L * h->cfg.L * sizeof(double), st);
+  if (e != hipSuccess) return INSTANT_E_HIP;
+  return status;
+}
+
+INSTANT_API instant_status instant_compress_fwd(instant_layer* h, const void* x, int32_t B, void* xhat,
+                                                void* stream) {
+  if (!h || !x || !xhat || B < 1) return INSTANT_E_ARG;
+  if (B > h->cfg.B_max) return INSTANT_E_SHAPE;
+  if (h->active < 0) return INSTANT_E_STATE;
+  const int a = h->active;
+  return hip_ok(launch_proj(h->bf16, h->PQ(a), h->lay.ldL, h->Rx, h->Rx, x, B, h->cfg.L, h->cfg.Cx, xhat, nullptr,
+                            S(stream)));
+}
+
+INSTANT_API instant_status instant_backward(instant_layer* h, const void* xhat, const void* gy, const void* w,
+                                            int32_t B, void* gw, void* gx, void* stream) {
+  if (!h || !xhat || !gy || !w || !gw || !gx || B < 1) return INSTANT_E_ARG;
+  if (B > h->cfg.B_max) return INSTANT_E_SHAPE;
+  if (h->active < 0) return INSTANT_E_STATE;
+  const int a = h->active;
+  const int L = h->cfg.L, Cx = h->cfg.Cx, Cy = h->cfg.Cy, Rx = h->Rx, Ry = h->Ry;
+  hipStream_t st = S(stream);
+  void* Pgy = h->ws + h->lay.Pgy;
+  void* Qgy = h->ws + h->lay.Qgy;
+  void* gxh = h->ws + h->lay.gxh;
+  // [P; Q] gy_b from one pass over gy
+  hipError_t e = launch_proj(h->bf16, h->PQ(a), h->lay.ldL, Rx + Ry, Rx, gy, B, L, Cy, Pgy, Qgy, st);
+  // g_w = sum_b (P gy_b)^T x_hat_b: M = Cy, N = Cx, K = B * Rx
+  if (e == hipSuccess) e = launch_gemm(h->bf16, true, Pgy, Cy, 0, xhat, Cx, 0, gw, Cx, 0, 1, Cy, Cx, B * Rx, st);
+  // g_hat_x = (Q gy) w: M = B * Ry, N = Cx, K = Cy
+  if (e == hipSuccess) e = launch_gemm(h->bf16, false, Qgy, Cy, 0, w, Cx, 0, gxh, Cx, 0, 1, B * Ry, Cx, Cy, st);
+  // g_x_b = Q^T g_hat_x_b
+  if (e == hipSuccess) e = launch_expand(h->bf16, h->Qt(a), LD_QT, gxh, B, Ry, L, Cx, gx, st);
+  return hip_ok(e);
+}
+
+INSTANT_API instant_status instant_query(instant_layer* h, instant_info* out) {
+  if (!h || !out) return INSTANT_E_ARG;
+  *out = h->info;
+  return h->last;
+}
+
+INSTANT_API instant_status instant_set_projections(instant_layer* h, const float* P, int32_t Rx, const float* Q,
+                                                   int32_t Ry, void* stream) {
+  if (!h || !P || !Q) return INSTANT_E_ARG;
+  if (Rx < 1 || Ry < 1 || Rx > h->cfg.R_max || Ry > h->cfg.R_max) return INSTANT_E_SHAPE;
+  hipStream_t st = S(stream);
+  const int t = (h->active == 0) ? 1 : 0;
+  const size_t L = h->cfg.L;
+  hipError_t e = hipMemcpyAsync(h->P32(t), P, (size_t)Rx * L * sizeof(float), hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(h->Q32(t), Q, (size_t)Ry * L * sizeof(float), hipMemcpyDeviceToDevice, st);
+  const int r[2] = {Rx, Ry};
+  if (e == hipSuccess) e = launch_fill_i32(h->rank_dev(), r, 2, st);
+  if (e == hipSuccess)
+    e = launch_build_io(h->bf16, h->P32(t), h->Q32(t), h->rank_dev(), h->rank_dev() + 1, h->cfg.L, h->lay.ldL,
+                        h->cfg.R_max, h->PQ(t), h->Qt(t), LD_QT, st);
+  if (e != hipSuccess) return INSTANT_E_HIP;
+  h->active = t;
+  h->Rx = Rx;
+  h->Ry = Ry;
+  h->info.Rx = Rx;
+  h->info.Ry = Ry;
+  h->info.generation += 1;
+  return INSTANT_OK;
+}
+
+INSTANT_API instant_status instant_get_projections(instant_layer* h, float* P, float* Q, float* sigma_x,
+                                                   float* sigma_g, void* stream) {
+  if (!h) return INSTANT_E_ARG;
+  if ((P || Q) && h->active < 0) return INSTANT_E_STATE;
+  hipStream_t st = S(stream);
+  const size_t L = h->cfg.L;
+  hipError_t e = hipSuccess;
+  if (P) e = hipMemcpyAsync(P, h->P32(h->active), (size_t)h->Rx * L * sizeof(float), hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess && Q)
+    e = hipMemcpyAsync(Q, h->Q32(h->active), (size_t)h->Ry * L * sizeof(float), hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess && sigma_x)
+    e = hipMemcpyAsync(sigma_x, h->ws + h->lay.sig_x, L * sizeof(float), hipMemcpyDeviceToDevice, st);
+  if (e == hipSuccess && sigma_g)
+    e = hipMemcpyAsync(sigma_g, h->ws + h->lay.sig_g, L * sizeof(float), hipMemcpyDeviceToDevice, st);
+  return hip_ok(e);
+}
+
+INSTANT_API instant_status instant_get_statistics(instant_layer* h, double* C_X, double* C_G, void* stream) {
+  if (!h) return INSTANT_E_ARG;
+  if ((C_X && h->nx == 0) || (C_G && h->ng == 0)) return INSTANT_E_STATE;
+  hipError_t e = hipSuccess;
+  if (C_X) e = launch_stat_mean(h->SX(), 1.0 / (double)h->nx, h->cfg.L, C_X, S(stream));
+  if (e == hipSuccess && C_G) e = launch_stat_mean(h->SG(), 1.0 / (double)h->ng, h->cfg.L, C_G, S(stream));
+  return hip_ok(e);
+}
+
+INSTANT_API const char* instant_status_str(instant_status s) {
+  switch (s) {
+    case INSTANT_OK: return "INSTANT_OK";
+    case INSTANT_E_ARG: return "INSTANT_E_ARG";
+    case INSTANT_E_SHAPE: return "INSTANT_E_SHAPE";
+    case INSTANT_E_STATE: return "INSTANT_E_STATE";
+    case INSTANT_E_RANK: return "INSTANT_E_RANK";
+    case INSTANT_E_ENERGY: return "INSTANT_E_ENERGY";
+    case INSTANT_E_NONFINITE: return "INSTANT_E_NONFINITE";
+    case INSTANT_E_NOCONV: return "INSTANT_E_NOCONV";
+    case INSTANT_E_HIP: return "INSTANT_E_HIP";
+  }
+  return "INSTANT_E_UNKNOWN";
+}

@@ -1,0 +1,67 @@
+// Host-side launchers of the INSTANT kernels. Each returns the launch status; all
+// work is enqueued on `st`. Pointers are device pointers; the I/O dtype is bf16
+// when `bf16_io` is true, float32 otherwise.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace instant {
+
+// Out[b][m][c] = sum_l A[m][l] X[b][l][c]; rows m < M0 to out0 [B][M0][C], the rest
+// to out1 [B][M-M0][C]. A: [M][ldA], zero beyond column L. M <= 128.
+hipError_t launch_proj(bool bf16_io, const void* A, int ldA, int M, int M0, const void* X, int B, int L, int C,
+                       void* out0, void* out1, hipStream_t st);
+
+// Cm[m][n] = sum_k A(m,k) B[k][n] per batch entry z (pointer strides sA, sB, sC in
+// elements). a_trans: A stored [K][lda] instead of [M][lda]. M, N multiples of 4 / 8.
+hipError_t launch_gemm(bool bf16_io, bool a_trans, const void* A, int lda, size_t sA, const void* Bm, int ldb,
+                       size_t sB, void* Cm, int ldc, size_t sC, int batch, int M, int N, int K, hipStream_t st);
+
+// Out[b][l][c] = sum_{r<R} At[l][r] Bz[b][r][c]; At: [L][ldA], zero beyond column R.
+hipError_t launch_expand(bool bf16_io, const void* At, int ldA, const void* Bz, int B, int R, int L, int C,
+                         void* out, hipStream_t st);
+
+// ---- calibration ([KD1], [KD2])
+
+// Upper-triangle tile partial sums of sum_b X_b X_b^T over `nsplit` slices of the
+// batch*channel reduction, written as float32 to part [nsplit][ntiles][64*64].
+hipError_t launch_syrk(bool bf16_io, const void* X, int B, int L, int C, int nsplit, float* part, hipStream_t st);
+// S[i][j] += sum_s part[s] (fixed order) for the upper-triangle tiles.
+hipError_t launch_syrk_reduce(const float* part, int nsplit, int L, double* S, hipStream_t st);
+int syrk_tiles(int L);
+
+// Eigen-decomposition of both statistics (C = S * inv_n, float64 upper-triangle sums)
+// by blocked one-sided Jacobi, then truncation, compensation and the float32
+// projections P32 [Rx][L] / Q32 [Ry][L], the descending spectra and the per-side
+// device info blocks (int32 slots: status, k, R, c bits, kept (f64), kept_k (f64)).
+// Synchronous: reads the convergence flags once per sweep. host_flags receives
+// [offmax x2, active x2, sweeps x2, converged x2, nonfinite x2].
+struct EigOut {
+  float eps;
+  int p, comp, R_max;
+  float* P32;
+  float* Q32;
+  float* sigma_x;
+  float* sigma_g;
+  int* info_x;
+  int* info_g;
+};
+constexpr int INFO_WORDS = 8;
+size_t eig_workspace_bytes(int L);
+hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv_ng, int L, int max_sweeps,
+                   void* work, const EigOut& out, int host_flags[10], hipStream_t st);
+
+// I/O-dtype copies of the active projections: PQ [2*R_max][ldL] (rows [0,Rx) = P,
+// [Rx,Rx+Ry) = Q, zero elsewhere) and Qt [L][ldQt] (zero beyond Ry).
+hipError_t launch_build_io(bool bf16_io, const float* P32, const float* Q32, const int* dRx, const int* dRy, int L,
+                           int ldL, int R_max, void* PQ, void* Qt, int ldQt, hipStream_t st);
+
+// out[i][j] = S[min][max] * inv_n for the full L x L matrix (float64).
+hipError_t launch_stat_mean(const double* S, double inv_n, int L, double* out, hipStream_t st);
+
+hipError_t launch_fill_i32(int* dst, const int* values, int n, hipStream_t st);
+hipError_t launch_zero(void* dst, size_t bytes, hipStream_t st);
+
+}  // namespace instant

@@ -1,0 +1,80 @@
+"""The C-ABI library loads and exports every entry point include/instant.h declares;
+host-side argument checks answer without touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "instant.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(instant_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("instant_calibrate", "instant_compress_fwd", "instant_backward"):
+        assert required in names
+    assert len(names) == 11
+
+
+def test_library_exports_every_declared_symbol():
+    import rank_compressed_backprop_amd as rcb
+    lib = ctypes.CDLL(rcb.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(rcb.EXPORTED)
+
+
+def test_status_strings():
+    import rank_compressed_backprop_amd as rcb
+    assert rcb.instant_status_str(rcb.INSTANT_OK) == "INSTANT_OK"
+    assert rcb.instant_status_str(rcb.INSTANT_E_RANK) == "INSTANT_E_RANK"
+    assert rcb.instant_status_str(99) == "INSTANT_E_UNKNOWN"
+
+
+def test_workspace_bytes_validates_config():
+    import rank_compressed_backprop_amd as rcb
+    good = rcb.make_config(512, 768, 768, 32, R_max=64, p=2)
+    n = rcb.instant_workspace_bytes(good)
+    assert n > 2 * 512 * 512 * 8  # at least the two float64 statistic sums
+    bad = [
+        dict(L=0), dict(L=5000), dict(Cx=12), dict(Cy=0), dict(B_max=0), dict(R_max=65),
+        dict(eps=0.0), dict(eps=1.5), dict(dtype=7), dict(comp=5), dict(max_sweeps=0), dict(p=-1),
+    ]
+    for change in bad:
+        cfg = rcb.make_config(512, 768, 768, 32, R_max=64, p=2)
+        for k, v in change.items():
+            setattr(cfg, k, v)
+        assert rcb.instant_workspace_bytes(cfg) == 0, change
+    # R_max is clamped to L by make_config; the raw struct may not exceed L
+    cfg = rcb.make_config(16, 8, 8, 1, R_max=64)
+    assert cfg.R_max == 16
+    cfg.R_max = 17
+    assert rcb.instant_workspace_bytes(cfg) == 0
+
+
+def test_host_errors_have_no_side_effects():
+    import rank_compressed_backprop_amd as rcb
+    cfg = rcb.make_config(64, 64, 64, 2, dtype="fp32")
+    # null workspace / misaligned workspace are refused before any device call
+    s, h = rcb.instant_create(cfg, 0, 0)
+    assert s == rcb.INSTANT_E_ARG
+    s, h = rcb.instant_create(cfg, 1000 * 256 + 8, 0)
+    assert s == rcb.INSTANT_E_ARG
+    bad = rcb.make_config(64, 64, 64, 2, dtype="fp32")
+    bad.eps = 2.0
+    s, h = rcb.instant_create(bad, 256 * 1000, 0)
+    assert s == rcb.INSTANT_E_ARG
+    # calls on a NULL handle
+    assert rcb.instant_calibrate(None, None, None, 1, 0, 0) == rcb.INSTANT_E_ARG
+    assert rcb.instant_compress_fwd(None, 8, 1, 8, 0) == rcb.INSTANT_E_ARG
+    assert rcb.instant_backward(None, 8, 8, 8, 1, 8, 8, 0) == rcb.INSTANT_E_ARG
+    s, _ = rcb.instant_query(None)
+    assert s == rcb.INSTANT_E_ARG
+    assert rcb.instant_destroy(None) == rcb.INSTANT_E_ARG

@@ -1,0 +1,209 @@
+"""GPU parity of the calibration (statistics, Jacobi eigen-decomposition, truncation,
+compensation) and of the end-to-end path against the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+COMP = {"paper": O.COMP_PAPER, "none": O.COMP_NONE, "ratio": O.COMP_RATIO}
+
+
+def _calibrate_both(wl, layer, comp="paper", R_max=64, n_cal=None, max_sweeps=30):
+    import rank_compressed_backprop_amd as rcb
+    from gpu_util import to_dev
+    ly = wl.layer(layer)
+    n_cal = n_cal or wl.n_cal
+    lay = rcb.InstantLayer(rcb.make_config(wl.L, ly.Cx, ly.Cy, wl.B, R_max=R_max, p=wl.p, eps=wl.eps,
+                                           dtype=wl.dtype, comp=comp, max_sweeps=max_sweeps))
+    xa, ga = O.Accumulator(wl.L), O.Accumulator(wl.L)
+    for t in range(n_cal):
+        d = W.make_layer_batch(wl, layer, t)
+        xa.add(d["x64"])
+        ga.add(d["gy64"])
+        assert lay.calibrate(to_dev(d["x"], wl.dtype), to_dev(d["gy"], wl.dtype), wl.B, finalize=False) == 0
+    CX = torch.empty((wl.L, wl.L), dtype=torch.float64, device="cuda")
+    CG = torch.empty((wl.L, wl.L), dtype=torch.float64, device="cuda")
+    lay.get_statistics(CX, CG)
+    torch.cuda.synchronize()
+    status = lay.calibrate(None, None, 0, finalize=True)
+    return lay, status, (xa, ga), (CX.cpu().numpy(), CG.cpu().numpy())
+
+
+CAL_CASES = [("tiny", "main", "paper"), ("tiny", "main", "ratio"), ("bert_attn", "main", "paper"),
+             ("bert_attn", "main", "none"), ("effformer", "up", "paper"), ("effformer", "down", "paper"),
+             ("bert_ffn", "up", "paper"), ("bert_ffn", "down", "paper")]
+
+
+@pytest.mark.parametrize("name,layer,comp", CAL_CASES)
+def test_calibration_and_end_to_end(name, layer, comp):
+    import rank_compressed_backprop_amd as rcb
+    from gpu_util import TOL, empty, from_dev, rel, to_dev
+    wl = W.get_workload(name)
+    ly = wl.layer(layer)
+    print(f"[calibration] {name}/{layer} comp={comp} L={wl.L}", flush=True)
+    lay, status, (xa, ga), (CX_g, CG_g) = _calibrate_both(wl, layer, comp)
+    assert status == rcb.INSTANT_OK, rcb.instant_status_str(status)
+
+    # statistics: float32 tile sums of exact products, float64 across slices and batches
+    e_cx, e_cg = rel(CX_g, xa.mean()), rel(CG_g, ga.mean())
+    print(f"  stats rel err C_X {e_cx:.2e} C_G {e_cg:.2e}", flush=True)
+    assert e_cx < 1e-5 and e_cg < 1e-5
+
+    ox = O.calibrate_side(xa.mean(), wl.eps, wl.p, COMP[comp], 64)
+    og = O.calibrate_side(ga.mean(), wl.eps, wl.p, COMP[comp], 64)
+    assert ox["status"] == O.OK and og["status"] == O.OK
+    # the integer decisions are well defined only with a margin at the threshold
+    assert ox["margin"] >= 1e-4 and og["margin"] >= 1e-4
+    s, info = lay.query()
+    print(f"  gpu k/R x {info.kx}/{info.Rx} g {info.ky}/{info.Ry} sweeps {info.sweeps_x}/{info.sweeps_g}; "
+          f"oracle x {ox['k']}/{ox['R']} g {og['k']}/{og['R']}", flush=True)
+    assert (info.kx, info.Rx, info.ky, info.Ry) == (ox["k"], ox["R"], og["k"], og["R"])
+
+    Rx, Ry = info.Rx, info.Ry
+    P_g = torch.empty((Rx, wl.L), device="cuda")
+    Q_g = torch.empty((Ry, wl.L), device="cuda")
+    sx = torch.empty(wl.L, device="cuda")
+    sg = torch.empty(wl.L, device="cuda")
+    lay.get_projections(P_g, Q_g, sx, sg)
+    torch.cuda.synchronize()
+    P_g, Q_g = P_g.cpu().numpy().astype(np.float64), Q_g.cpu().numpy().astype(np.float64)
+    sx, sg = sx.cpu().numpy().astype(np.float64), sg.cpu().numpy().astype(np.float64)
+    # singular values: the kept ones and the total energy
+    for sgpu, o in ((sx, ox), (sg, og)):
+        R = o["R"]
+        e_sig = np.max(np.abs(sgpu[:R] - o["sigma"][:R]) / o["sigma"][0])
+        e_E = abs(np.sum(sgpu ** 2) - o["E"]) / o["E"]
+        print(f"  sigma max err {e_sig:.2e} (of sigma_0), energy rel err {e_E:.2e}", flush=True)
+        # float32 columns: each of the ~sweeps*(L/8) rotations of a column rounds it at 2^-24,
+        # a random walk of about sqrt(#rotations) * 2^-24 <= 1e-5 here; 1e-4 leaves room and
+        # is still ten times under the margin the integer decision is required to have
+        assert e_sig < 1e-4 and e_E < 1e-4
+    # compensation scalars and the projectors (gauge-invariant)
+    assert abs(info.cP - ox["c"]) <= 1e-5 * ox["c"]
+    assert abs(info.cQ - og["c"]) <= 1e-5 * og["c"]
+    for Pg, o in ((P_g, ox), (Q_g, og)):
+        Po = o["P"]
+        d = rel(Pg.T @ Pg, Po.T @ Po)
+        print(f"  projector distance {d:.2e} (gap {o['gap']:.1e})", flush=True)
+        assert d < 1e-3
+        # with canonical signs on both sides the rows themselves agree
+        assert rel(Pg, Po) < 2e-3
+
+    # end to end on a fresh batch: the GPU's own projections against the oracle's
+    d = W.make_layer_batch(wl, layer, wl.n_cal, with_w=True)
+    x, gy, w = to_dev(d["x"], wl.dtype), to_dev(d["gy"], wl.dtype), to_dev(d["w"], wl.dtype)
+    xhat = empty((wl.B, Rx, ly.Cx), wl.dtype)
+    gw = empty((ly.Cy, ly.Cx), wl.dtype)
+    gx = empty((wl.B, wl.L, ly.Cx), wl.dtype)
+    lay.compress_fwd(x, wl.B, xhat)
+    lay.backward(xhat, gy, w, wl.B, gw, gx)
+    torch.cuda.synchronize()
+    xh_o = O.compress(ox["P"], d["x64"])
+    out = O.backward(ox["P"], og["P"], xh_o, d["gy64"], d["w64"])
+    tol = TOL[wl.dtype]
+    e = (rel(from_dev(xhat, wl.dtype), xh_o), rel(from_dev(gw, wl.dtype), out["gw"]),
+         rel(from_dev(gx, wl.dtype), out["gx"]))
+    print("  end-to-end rel err xhat %.2e gw %.2e gx %.2e (tol %g)" % (*e, tol), flush=True)
+    assert max(e) <= tol
+
+
+def test_full_rank_identity_on_gpu():
+    """R = L with uncompensated projections: P^T P = I, so the low-rank gradients are
+    the exact g_w = sum gy^T x and g_x = gy w (fp32, L = 64)."""
+    import rank_compressed_backprop_amd as rcb
+    from gpu_util import empty, from_dev, rel, to_dev
+    rng = np.random.default_rng(11)
+    B, L, C = 4, 64, 64
+    lay = rcb.InstantLayer(rcb.make_config(L, C, C, B, R_max=64, p=64, eps=0.95, dtype="fp32", comp="none"))
+    x = rng.standard_normal((B, L, C)).astype(np.float32)
+    gy = rng.standard_normal((B, L, C)).astype(np.float32)
+    w = (0.1 * rng.standard_normal((C, C))).astype(np.float32)
+    assert lay.calibrate(to_dev(x, "fp32"), to_dev(gy, "fp32"), B, finalize=True) == 0
+    s, info = lay.query()
+    assert info.Rx == L and info.Ry == L
+    xh, gw, gx = empty((B, L, C), "fp32"), empty((C, C), "fp32"), empty((B, L, C), "fp32")
+    xd, gyd, wd = to_dev(x, "fp32"), to_dev(gy, "fp32"), to_dev(w, "fp32")
+    lay.compress_fwd(xd, B, xh)
+    lay.backward(xh, gyd, wd, B, gw, gx)
+    torch.cuda.synchronize()
+    ex = O.exact_backward(x, gy, w)
+    e_gw, e_gx = rel(from_dev(gw, "fp32"), ex["gw"]), rel(from_dev(gx, "fp32"), ex["gx"])
+    print(f"  full-rank identity rel err gw {e_gw:.2e} gx {e_gx:.2e}", flush=True)
+    assert e_gw < 1e-4 and e_gx < 1e-4
+
+
+def _fresh_layer(dtype="fp32", L=32, C=16, B=2, **kw):
+    import rank_compressed_backprop_amd as rcb
+    return rcb.InstantLayer(rcb.make_config(L, C, C, B, dtype=dtype, **kw))
+
+
+def test_zero_energy_is_reported_and_keeps_old_projections():
+    import rank_compressed_backprop_amd as rcb
+    from gpu_util import empty, to_dev
+    lay = _fresh_layer()
+    P = torch.eye(32, device="cuda")[:3].contiguous()
+    lay.set_projections(P, 3, P, 3)
+    z = to_dev(np.zeros((2, 32, 16), np.float32), "fp32")
+    g = to_dev(np.random.default_rng(1).standard_normal((2, 32, 16)).astype(np.float32), "fp32")
+    assert lay.calibrate(z, g, 2, finalize=True) == rcb.INSTANT_E_ENERGY
+    s, info = lay.query()
+    assert s == rcb.INSTANT_E_ENERGY and info.Rx == 3
+    xh = empty((2, 3, 16), "fp32")
+    lay.compress_fwd(g, 2, xh)  # the old projections are still active
+    torch.cuda.synchronize()
+
+
+def test_rank_overflow_is_reported():
+    import rank_compressed_backprop_amd as rcb
+    from gpu_util import to_dev
+    wl = W.get_workload("bert_attn")
+    lay = rcb.InstantLayer(rcb.make_config(wl.L, 768, 768, wl.B, R_max=4, p=wl.p, dtype="bf16"))
+    d = W.make_layer_batch(wl, 0, 0)
+    assert lay.calibrate(to_dev(d["x"], "bf16"), to_dev(d["gy"], "bf16"), wl.B, finalize=True) == rcb.INSTANT_E_RANK
+
+
+def test_nonfinite_statistics_are_reported():
+    import rank_compressed_backprop_amd as rcb
+    from gpu_util import to_dev
+    lay = _fresh_layer()
+    x = np.random.default_rng(2).standard_normal((2, 32, 16)).astype(np.float32)
+    x[1, 5, 3] = np.nan
+    assert lay.calibrate(to_dev(x, "fp32"), to_dev(np.abs(x[::-1]).copy(), "fp32"), 2,
+                         finalize=True) == rcb.INSTANT_E_NONFINITE
+
+
+def test_no_convergence_is_reported():
+    import rank_compressed_backprop_amd as rcb
+    from gpu_util import to_dev
+    lay = _fresh_layer(L=64, C=64, max_sweeps=1)
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((2, 64, 64)).astype(np.float32)
+    assert lay.calibrate(to_dev(x, "fp32"), to_dev(x, "fp32"), 2, finalize=True) == rcb.INSTANT_E_NOCONV
+
+
+def test_hand_built_spectrum_through_gpu_eigensolver():
+    """C = H diag(lam) H^T with a normalised Hadamard H: the GPU must recover lam and
+    pick the brute-force k; statistics are fed as samples t_b = H diag(sqrt(lam)) (scaled)."""
+    import rank_compressed_backprop_amd as rcb
+    from gpu_util import to_dev
+    from pins import brute_force_k, hadamard
+    L = 64
+    H = hadamard(L)
+    lam = 0.7 ** np.arange(L)
+    eps, p = 0.9, 3
+    # one sample whose t t^T equals L * C when its L channels are H diag(sqrt(lam)) * sqrt(L)
+    t = (H * np.sqrt(lam)[None, :]).astype(np.float32)[None]  # [1, L, L]: t t^T = H diag(lam) H^T
+    lay = rcb.InstantLayer(rcb.make_config(L, L, L, 1, p=p, eps=eps, dtype="fp32", comp="none"))
+    assert lay.calibrate(to_dev(t, "fp32"), to_dev(t, "fp32"), 1, finalize=True) == 0
+    s, info = lay.query()
+    kb = brute_force_k(lam, eps)
+    assert info.kx == kb and info.Rx == min(kb + p, L)
+    sx = torch.empty(L, device="cuda")
+    lay.get_projections(None, None, sx, None)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(sx.cpu().numpy() - lam)) < 1e-5
