@@ -36,7 +36,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="bert_attn")
-    ap.add_argument("--batches", type=int, default=16, help="distinct resident batches cycled through")
+    ap.add_argument("--batches", type=int, default=32,
+                    help="distinct resident batches cycled through (more than N_cal, so consecutive "
+                         "calibration windows see different statistics)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=8, help="samples of a batch the oracle times")
     return ap.parse_args()

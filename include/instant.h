@@ -36,7 +36,7 @@
  *   - The I/O dtype (x, gy, w, xhat, gw, gx) is fixed per handle: float32 or
  *     bfloat16. Accumulation is float32; statistics are summed in float64 across
  *     batches.
- *   - Cx and Cy must be multiples of 8; L >= 1; 1 <= R_max <= 64 and R_max <= L.
+ *   - Cx and Cy must be multiples of 8; 1 <= L <= 2048; 1 <= R_max <= 64 and R_max <= L.
  *   - A handle is used from one stream at a time; calls are not re-entrant.
  */
 #ifndef INSTANT_H_

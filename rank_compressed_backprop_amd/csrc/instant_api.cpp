@@ -20,7 +20,7 @@ namespace {
 
 using namespace instant;
 
-constexpr int MAX_L = 4096;
+constexpr int MAX_L = 2048;  // a Jacobi pair stages 16 columns of L floats in LDS
 constexpr int MAX_R = 64;
 constexpr int LD_QT = 64;
 constexpr int SYRK_TARGET_BLOCKS = 1024;
@@ -92,6 +92,7 @@ struct instant_layer {
   char* ws;
   Layout lay;
   int active;  // projection buffer in use, -1 before the first one
+  bool warm;   // the eigensolver's accumulated rotation from the last finalize is usable
   int Rx, Ry;
   int64_t nx, ng;
   instant_info info;
@@ -140,6 +141,7 @@ INSTANT_API instant_status instant_create(instant_layer** h, const instant_confi
   L->ws = (char*)workspace;
   L->lay = layout_of(cfg);
   L->active = -1;
+  L->warm = false;
   L->Rx = L->Ry = 0;
   L->nx = L->ng = 0;
   std::memset(&L->info, 0, sizeof(L->info));
@@ -195,10 +197,13 @@ INSTANT_API instant_status instant_calibrate(instant_layer* h, const void* x, co
   out.sigma_g = (float*)(h->ws + h->lay.sig_g);
   out.info_x = h->info_dev();
   out.info_g = h->info_dev() + INFO_WORDS;
-  int flags[10];
+  int flags[EIG_HOST_FLAGS];
   hipError_t e = run_eig(h->SX(), h->SG(), 1.0 / (double)h->nx, 1.0 / (double)h->ng, h->cfg.L, h->cfg.max_sweeps,
-                         h->ws + h->lay.eig, out, flags, st);
-  if (e != hipSuccess) return INSTANT_E_HIP;
+                         h->warm, h->ws + h->lay.eig, out, flags, st);
+  if (e != hipSuccess) {
+    h->warm = false;
+    return INSTANT_E_HIP;
+  }
   int info[2 * INFO_WORDS];
   e = hipMemcpyAsync(info, h->info_dev(), sizeof(info), hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
@@ -210,8 +215,8 @@ INSTANT_API instant_status instant_calibrate(instant_layer* h, const void* x, co
   instant_info& I = h->info;
   I.kx = ix[1];
   I.ky = ig[1];
-  I.sweeps_x = flags[4];
-  I.sweeps_g = flags[5];
+  I.sweeps_x = flags[EIGF_SWEEPS];
+  I.sweeps_g = flags[EIGF_SWEEPS + 1];
   I.status = status;
   float c;
   std::memcpy(&c, &ix[3], 4);
@@ -234,6 +239,8 @@ INSTANT_API instant_status instant_calibrate(instant_layer* h, const void* x, co
     I.generation += 1;
   }
   h->last = status;
+  // a failed decomposition may leave the accumulated rotation unusable: restart cold
+  h->warm = (status == INSTANT_OK || status == INSTANT_E_RANK);
   // the statistics window is consumed whatever the outcome
   h->nx = h->ng = 0;
   e = launch_zero(h->SX(), (size_t)h->cfg.L * h->cfg.L * sizeof(double), st);

@@ -1,0 +1,760 @@
+// Eigen-decomposition and truncation of the INSTANT statistics (notes "INSTANT:
+// Compressing Gradients and Activations for Resource-Efficient Training", sections
+// 关键设计 1: the singular vectors of C_X = E[x x^T] / C_G = E[g_y g_y^T]; 关键设计 2:
+// energy threshold, oversampling, compensation).
+//
+// Blocked one-sided (Hestenes) Jacobi. The columns of W = C V0 (V0 orthogonal: the
+// identity on the first calibration, the previous calibration's accumulated rotation
+// afterwards) are orthogonalised in blocks of 8. A round pairs the blocks by a
+// round-robin tournament; each pair forms the 16x16 Gram matrix of its columns on the
+// matrix cores, diagonalises it by cyclic Jacobi in float64 and rotates its columns
+// (and the same columns of the accumulated V). At convergence W = U Sigma, so the
+// column norms are the singular values of C (its eigenvalues, C being PSD) and the
+// normalised columns its eigenvectors; V holds the rotation that starts the next
+// calibration.
+//
+// One cooperative launch runs every sweep. Pairs synchronise through per-block
+// version counters (a pair waits only for the two column blocks it reads), and all
+// blocks meet once per sweep to agree on convergence. Every wait is bounded: a
+// timeout raises a global abort flag that releases every other wait, so the grid
+// always drains.
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace instant {
+
+constexpr int JB = 8;               // columns per Jacobi block
+constexpr int JAC_MAX_LDW = 2048;   // the 16 columns of a pair are staged in LDS (128 KB)
+// Columns whose squared norm is below NOISE_REL * ||C||_F^2 lie under float32 resolution
+// (sigma below 1e-5 of the total): their pairings are neither rotated nor counted.
+constexpr double NOISE_REL = 1e-10;
+constexpr long SPIN_LIMIT = 1L << 24;  // ~1 s of polling before a wait gives up
+
+struct EigLayout {
+  int ldw, nb, ncols;
+  size_t wbytes, vbytes, nrmbytes, verbytes, colbytes;
+};
+
+static size_t al256(size_t n) { return (n + 255) / 256 * 256; }
+
+static EigLayout eig_layout(int L) {
+  EigLayout e;
+  e.ldw = (L + 15) / 16 * 16;
+  int nb = (L + JB - 1) / JB;
+  if (nb < 2) nb = 2;
+  if (nb & 1) ++nb;
+  e.nb = nb;
+  e.ncols = nb * JB;
+  e.wbytes = al256((size_t)e.ncols * e.ldw * sizeof(float));
+  e.vbytes = al256((size_t)e.ncols * e.ldw * sizeof(double));
+  e.nrmbytes = al256((size_t)L * sizeof(float));
+  e.verbytes = al256((size_t)2 * nb * sizeof(int));
+  e.colbytes = al256((size_t)e.ncols * sizeof(int));
+  return e;
+}
+
+// flags block (int32 slots)
+constexpr int F_OFFMAX = 0;     // [3 slots][2 sides] float bits
+constexpr int F_SWEEPS = 6;     // [2]
+constexpr int F_CONV = 8;       // [2]
+constexpr int F_BAD = 10;       // [2] non-finite statistics
+constexpr int F_SCALE = 12;     // 2 doubles: ||C||_F^2 per side
+constexpr int F_BARRIER = 16;   // sweep barrier arrivals
+constexpr int F_ABORT = 17;     // a bounded wait timed out
+constexpr int F_NALIVE = 18;    // [2] columns above the noise floor
+constexpr size_t EIG_FLAGS_BYTES = 256;
+
+struct EigBufs {
+  float* W[2];
+  float* Wtmp;      // statistic in float32 before the warm start product
+  double* V[2];
+  float* nrm[2];
+  int* flags;
+  int* version;     // [2][nb]
+  int* cols[2];     // [ncols] column order: columns above the noise floor first
+};
+
+static EigBufs eig_bufs(void* work, const EigLayout& e) {
+  EigBufs b;
+  char* p = (char*)work;
+  b.W[0] = (float*)p;
+  p += e.wbytes;
+  b.W[1] = (float*)p;
+  p += e.wbytes;
+  b.Wtmp = (float*)p;
+  p += e.wbytes;
+  b.V[0] = (double*)p;
+  p += e.vbytes;
+  b.V[1] = (double*)p;
+  p += e.vbytes;
+  b.nrm[0] = (float*)p;
+  p += e.nrmbytes;
+  b.nrm[1] = (float*)p;
+  p += e.nrmbytes;
+  b.flags = (int*)p;
+  p += EIG_FLAGS_BYTES;
+  b.version = (int*)p;
+  p += e.verbytes;
+  b.cols[0] = (int*)p;
+  p += e.colbytes;
+  b.cols[1] = (int*)p;
+  return b;
+}
+
+size_t eig_workspace_bytes(int L) {
+  const EigLayout e = eig_layout(L);
+  return 3 * e.wbytes + 2 * e.vbytes + 2 * e.nrmbytes + EIG_FLAGS_BYTES + e.verbytes + 2 * e.colbytes;
+}
+
+// ---------------------------------------------------------------------------- set-up kernels
+
+// W[c][r] = S[min(r,c)][max(r,c)] * inv_n (column-major, zero padding); flags non-finite sums.
+__global__ __launch_bounds__(256) void jacobi_prep_kernel(const double* __restrict__ S, double inv_n, int L, int ldw,
+                                                          float* __restrict__ W, int* __restrict__ bad) {
+  const int c = blockIdx.x;
+  for (int r = threadIdx.x; r < ldw; r += 256) {
+    float v = 0.0f;
+    if (r < L && c < L) {
+      const int i = r < c ? r : c;
+      const int j = r < c ? c : r;
+      const double d = S[(size_t)i * L + j] * inv_n;
+      if (!isfinite(d)) atomicOr(bad, 1);
+      v = (float)d;
+    }
+    W[(size_t)c * ldw + r] = v;
+  }
+}
+
+// V = I (column-major, ncols x ldw).
+__global__ __launch_bounds__(256) void identity_kernel(double* __restrict__ V, int ldw) {
+  const int c = blockIdx.x;
+  for (int r = threadIdx.x; r < ldw; r += 256) V[(size_t)c * ldw + r] = (r == c) ? 1.0 : 0.0;
+}
+
+// Warm start: W[c][r] = sum_k C[r][k] V[c][k] with C symmetric (float32, column-major in
+// Ct), V float64, float64 accumulation. 64x64 output tiles, k in chunks of 16 through LDS.
+__global__ __launch_bounds__(256) void warm_gemm_kernel(const float* __restrict__ Ct, const double* __restrict__ V,
+                                                        int L, int ldw, int ncols, float* __restrict__ W) {
+  __shared__ double Cs[16][65];
+  __shared__ double Vs[16][65];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tr = threadIdx.x & 15, tc = threadIdx.x >> 4;
+  double acc[4][4] = {};
+  for (int k0 = 0; k0 < L; k0 += 16) {
+    for (int e = threadIdx.x; e < 16 * 64; e += 256) {
+      const int kk = e >> 6, rr = e & 63;
+      const int k = k0 + kk;
+      Cs[kk][rr] = (k < L && r0 + rr < ldw) ? (double)Ct[(size_t)k * ldw + r0 + rr] : 0.0;
+      const int cc = e >> 4, k2 = e & 15;
+      Vs[k2][cc] = (k0 + k2 < L && c0 + cc < ncols) ? V[(size_t)(c0 + cc) * ldw + k0 + k2] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < 16; ++kk) {
+      double cr[4], vc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cr[i] = Cs[kk][tr + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vc[j] = Vs[kk][tc + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(cr[i], vc[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = r0 + tr + 16 * i;
+      const int c = c0 + tc + 16 * j;
+      if (r < ldw && c < ncols) W[(size_t)c * ldw + r] = (float)acc[i][j];
+    }
+}
+
+// Column norms of W: sigma_c = ||W[:, c]||, c < L.
+__global__ __launch_bounds__(64) void colnorm_kernel(const float* __restrict__ W, int ldw, int L,
+                                                     float* __restrict__ nrm) {
+  const int c = blockIdx.x;
+  const int lane = threadIdx.x;
+  float acc = 0.0f;
+  for (int r = lane; r < L; r += 64) {
+    const float v = W[(size_t)c * ldw + r];
+    acc += v * v;
+  }
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) nrm[c] = sqrtf(acc);
+}
+
+// ||W||_F^2 from the column norms, in a fixed order (one block).
+__global__ __launch_bounds__(256) void frob_kernel(const float* __restrict__ nrm, int L, double* __restrict__ out) {
+  __shared__ double red[256];
+  double acc = 0.0;
+  for (int c = threadIdx.x; c < L; c += 256) acc += (double)nrm[c] * (double)nrm[c];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = red[0];
+}
+
+// Deflation: columns whose squared norm is under the noise floor are left out of the
+// tournament (they would never be rotated). cols = [columns above the floor in index
+// order, then the others]; n_alive counts the first group. One block.
+__global__ __launch_bounds__(1024) void alive_kernel(const float* __restrict__ nrm, const double* __restrict__ scale,
+                                                     int L, int ncols, int* __restrict__ cols,
+                                                     int* __restrict__ n_alive) {
+  __shared__ int flag[2048];
+  __shared__ int pos[2048];
+  const double floor_g = NOISE_REL * *scale;
+  for (int c = threadIdx.x; c < ncols; c += 1024) {
+    const double n = c < L ? (double)nrm[c] : 0.0;
+    flag[c] = (c < L && n * n > floor_g) ? 1 : 0;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {  // ordered scan (ncols <= 2048)
+    int a = 0;
+    for (int c = 0; c < ncols; ++c) {
+      pos[c] = a;
+      a += flag[c];
+    }
+    *n_alive = a;
+    int d = a;
+    for (int c = 0; c < ncols; ++c) {
+      if (flag[c]) cols[pos[c]] = c;
+      else cols[d++] = c;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- Jacobi
+
+__device__ inline int tourney(int pos, int round, int nb) {
+  // circle method: position 0 fixed, the others rotate by `round`
+  return pos == 0 ? 0 : 1 + (pos - 1 + round) % (nb - 1);
+}
+
+struct JacobiArgs {
+  float* W[2];
+  double* V[2];
+  const double* scale;  // [2] ||C||_F^2, invariant under the rotations
+  unsigned* offmax;     // [3][2]
+  int* out;             // [0..1] sweeps, [2..3] converged
+  int* barrier;
+  int* abort;
+  int* version;         // [2][nb]
+  const int* cols[2];   // column order per side (alive columns first)
+  const int* n_alive;   // [2]
+  int L, ldw, nb, max_sweeps;
+  float tol, rot_tol;
+};
+
+struct JacobiSmem {
+  int col[16];
+  int partner[16];
+  float part[4][16][17];
+  double G[16][17];
+  double V[16][17];
+  double jd[16], jo[16];
+  int need;
+  int ok;
+};
+
+// LDS ordering inside one wave: every lane's earlier LDS access has completed.
+__device__ inline void wave_lds_sync() { __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ inline void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+// Wait until *p >= v. Gives up (raising the abort flag) after SPIN_LIMIT polls or as soon
+// as another block raised it.
+__device__ bool wait_geq(const int* p, int v, int* abort) {
+  for (long it = 0;; ++it) {
+    if (__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= v) return true;
+    if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return false;
+    if (it > SPIN_LIMIT) {
+      __hip_atomic_store(abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// One block pair of one side: stage the 16 columns in LDS, form their Gram matrix on the
+// matrix cores (float32), diagonalise it by cyclic Jacobi (one wave, float64), and rotate
+// the 16 columns of W and of the accumulated V.
+__device__ void jacobi_pair(const JacobiArgs& a, int side, int ba, int bb, int slot, JacobiSmem& sm, float* Y) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wave = threadIdx.x / WAVE;
+  float* __restrict__ W = a.W[side];
+  double* __restrict__ Vg = a.V[side];
+  if (threadIdx.x < 16) sm.col[threadIdx.x] = a.cols[side][(threadIdx.x < 8 ? ba : bb) * JB + (threadIdx.x & 7)];
+  __syncthreads();
+  const double floor_g = NOISE_REL * a.scale[side];
+
+  // stage the columns, every load issued before any is used
+  {
+    const int n4 = a.ldw / 4;
+    for (int i0 = threadIdx.x; i0 < 16 * n4; i0 += 256 * 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 256;
+        if (i < 16 * n4) v[u] = *reinterpret_cast<const f32x4*>(W + (size_t)sm.col[i / n4] * a.ldw + 4 * (i % n4));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 256;
+        if (i < 16 * n4) *reinterpret_cast<f32x4*>(&Y[(i / n4) * a.ldw + 4 * (i % n4)]) = v[u];
+      }
+    }
+  }
+  __syncthreads();
+
+  // G = Y^T Y: lane i reads four consecutive rows of column (i % 16), the four waves take
+  // alternate 16-row steps, LDS sums the four partial tiles
+  {
+    const float* __restrict__ cp = Y + (lane & 15) * a.ldw;
+    f32x4 acc = zero4();
+    for (int r0 = 16 * wave + 4 * (lane >> 4); r0 < a.ldw; r0 += 64) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(cp + r0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v[0], v[0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v[1], v[1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v[2], v[2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v[3], v[3], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sm.part[wave][4 * (lane >> 4) + v][lane & 15] = acc[v];
+  }
+  __syncthreads();
+
+  if (wave == 0) {
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = lane * 4 + e;
+      const int x = idx >> 4, y = idx & 15;
+      sm.G[x][y] = (double)sm.part[0][x][y] + (double)sm.part[1][x][y] + (double)sm.part[2][x][y] +
+                   (double)sm.part[3][x][y];
+      sm.V[x][y] = (x == y) ? 1.0 : 0.0;
+    }
+    wave_lds_sync();
+    // the pair's largest relative off-diagonal (columns above the noise floor only)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = lane * 4 + e;
+      const int x = idx >> 4, y = idx & 15;
+      if (x < y) {
+        const double gx = sm.G[x][x], gy = sm.G[y][y];
+        if (gx > floor_g && gy > floor_g) m = fmaxf(m, (float)(fabs(sm.G[x][y]) / sqrt(gx * gy)));
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (lane == 0) {
+      if (m > 0.0f) atomicMax(a.offmax + slot * 2 + side, __float_as_uint(m));
+      sm.need = m > a.rot_tol;
+    }
+    wave_lds_sync();
+
+    // Inner cyclic Jacobi, at most two sweeps per visit. Angles come from float32
+    // arithmetic; each (c, s) is renormalised in float64 so that every accumulated
+    // rotation is orthogonal to float64 precision.
+    for (int isweep = 0; isweep < 2 && sm.need; ++isweep) {
+      int rotated = 0;
+      for (int ir = 0; ir < 15; ++ir) {
+        if (lane < 8) {
+          const int p = tourney(lane, ir, 16);
+          const int q = tourney(15 - lane, ir, 16);
+          const double ad = sm.G[p][p], dd = sm.G[q][q], od = sm.G[p][q];
+          double c = 1.0, sn = 0.0;
+          if (ad > floor_g && dd > floor_g && fabs(od) > (double)a.rot_tol * sqrt(ad * dd)) {
+            const float zeta = (float)((dd - ad) / (2.0 * od));
+            const float t = copysignf(1.0f, zeta) / (fabsf(zeta) + sqrtf(1.0f + zeta * zeta));
+            const float cf = rsqrtf(1.0f + t * t);
+            c = (double)cf;
+            sn = (double)(t * cf);
+            const double dlt = c * c + sn * sn - 1.0;  // |dlt| ~ 1e-7
+            const double nrm = 1.0 - 0.5 * dlt + 0.375 * dlt * dlt;
+            c *= nrm;
+            sn *= nrm;
+            rotated = 1;
+          }
+          // new column p = c*p - s*q, new column q = s*p + c*q
+          sm.partner[p] = q;
+          sm.jd[p] = c;
+          sm.jo[p] = -sn;
+          sm.partner[q] = p;
+          sm.jd[q] = c;
+          sm.jo[q] = sn;
+        }
+        wave_lds_sync();
+        double gn[4], vn[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int idx = lane * 4 + e;
+          const int x = idx >> 4, y = idx & 15;
+          const int ox = sm.partner[x], oy = sm.partner[y];
+          const double jdx = sm.jd[x], jox = sm.jo[x], jdy = sm.jd[y], joy = sm.jo[y];
+          gn[e] = jdx * (jdy * sm.G[x][y] + joy * sm.G[x][oy]) + jox * (jdy * sm.G[ox][y] + joy * sm.G[ox][oy]);
+          vn[e] = sm.V[x][y] * jdy + sm.V[x][oy] * joy;
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int idx = lane * 4 + e;
+          sm.G[idx >> 4][idx & 15] = gn[e];
+          sm.V[idx >> 4][idx & 15] = vn[e];
+        }
+        wave_lds_sync();
+      }
+      // wave-uniform: every lane saw the same rotations
+      rotated = __shfl(rotated, 0) | __shfl(rotated, 1) | __shfl(rotated, 2) | __shfl(rotated, 3) |
+                __shfl(rotated, 4) | __shfl(rotated, 5) | __shfl(rotated, 6) | __shfl(rotated, 7);
+      if (!rotated) break;
+    }
+  }
+  __syncthreads();
+  if (!sm.need) return;
+
+  // Y <- Y V (W from LDS, float64 arithmetic) and V_acc <- V_acc V (float64 in memory)
+  for (int r = threadIdx.x; r < a.ldw; r += 256) {
+    float y[16];
+    double vv[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      y[q] = Y[q * a.ldw + r];
+      vv[q] = Vg[(size_t)sm.col[q] * a.ldw + r];
+    }
+    double acc[16], accv[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = accv[q] = 0.0;
+#pragma unroll 1
+    for (int p = 0; p < 16; ++p) {
+      const double yp = (double)y[p], vp = vv[p];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const double vpq = sm.V[p][q];  // LDS broadcast
+        acc[q] = fma(yp, vpq, acc[q]);
+        accv[q] = fma(vp, vpq, accv[q]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      W[(size_t)sm.col[q] * a.ldw + r] = (float)acc[q];
+      Vg[(size_t)sm.col[q] * a.ldw + r] = accv[q];
+    }
+  }
+}
+
+// Block b handles pair (b mod nb/2) of side (b div nb/2) in every round. Round r of the
+// whole run (all sweeps counted) may start on column blocks a, b once their version
+// counters reached r; the pair then raises both to r + 1. Once per sweep all blocks meet
+// at a counting barrier and read the same per-side maxima, so they take the same
+// decisions. The maxima rotate over three slots: slot (s+1) mod 3 is cleared during
+// sweep s, after every block has read it at the end of sweep s-2.
+__global__ __launch_bounds__(256) void jacobi_kernel(JacobiArgs a) {
+  __shared__ JacobiSmem sm;
+  extern __shared__ float Ydyn[];  // the pair's 16 columns, 16 * ldw floats
+  const int nbmax = a.nb;
+  const int side = blockIdx.x / (nbmax / 2);
+  const int pair = blockIdx.x % (nbmax / 2);
+  // this side's tournament: the alive columns, in blocks of 8, an even number of blocks
+  int nbs = (a.n_alive[side] + JB - 1) / JB;
+  if (nbs < 2) nbs = 2;
+  if (nbs & 1) ++nbs;
+  const bool mine = pair < nbs / 2;
+  int* ver = a.version + side * nbmax;
+  int active[2] = {1, 1};
+  int sweeps[2] = {0, 0};
+  bool aborted = false;
+  int rg = 0;  // this side's round index over the whole run
+  for (int sweep = 0; sweep < a.max_sweeps && (active[0] || active[1]); ++sweep) {
+    const int slot = sweep % 3;
+    if (blockIdx.x == 0 && threadIdx.x < 2) {
+      __hip_atomic_store(a.offmax + ((sweep + 1) % 3) * 2 + threadIdx.x, 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (active[side] && mine) {
+      for (int round = 0; round < nbs - 1; ++round, ++rg) {
+        const int ba = tourney(pair, round, nbs);
+        const int bb = tourney(nbs - 1 - pair, round, nbs);
+        if (threadIdx.x == 0) sm.ok = wait_geq(&ver[ba], rg, a.abort) && wait_geq(&ver[bb], rg, a.abort);
+        __syncthreads();
+        if (!sm.ok) {
+          aborted = true;
+          break;
+        }
+        acquire_agent();
+        jacobi_pair(a, side, ba, bb, slot, sm, Ydyn);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          __threadfence();
+          __hip_atomic_store(&ver[ba], rg + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(&ver[bb], rg + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    if (aborted) break;
+    // sweep barrier (every block of both sides, working or not)
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __threadfence();
+      __hip_atomic_fetch_add(a.barrier, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      sm.ok = wait_geq(a.barrier, (int)gridDim.x * (sweep + 1), a.abort);
+    }
+    __syncthreads();
+    if (!sm.ok) {
+      aborted = true;
+      break;
+    }
+    acquire_agent();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (active[s]) {
+        sweeps[s] += 1;
+        const unsigned bits = __hip_atomic_load(a.offmax + slot * 2 + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__uint_as_float(bits) <= a.tol) active[s] = 0;
+      }
+    }
+    __syncthreads();  // sm.ok is rewritten in the next sweep
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.out[0] = sweeps[0];
+    a.out[1] = sweeps[1];
+    a.out[2] = !active[0] && !aborted;
+    a.out[3] = !active[1] && !aborted;
+  }
+}
+
+// ---------------------------------------------------------------------------- truncation / build
+
+// Device-side info block of one side (int32 slots).
+// [0] status [1] k [2] R [3] c (float bits) [4..5] kept (double) [6..7] kept_k (double)
+constexpr int MAX_L = 2048;
+constexpr int INFO_STATUS = 0, INFO_K = 1, INFO_R = 2, INFO_C = 3, INFO_KEPT = 4, INFO_KEPTK = 6;
+
+// One block of 1024 threads: sort the L column norms (descending, ties by column index),
+// energy prefix in float64, truncation, compensation and P = c * U_R^T.
+__global__ __launch_bounds__(1024) void truncate_build_kernel(const float* __restrict__ W, int ldw, int L,
+                                                              const float* __restrict__ nrm, float eps, int p,
+                                                              int comp, int R_max, const int* __restrict__ bad,
+                                                              const int* __restrict__ converged,
+                                                              float* __restrict__ P32, float* __restrict__ sigma_out,
+                                                              int* __restrict__ info) {
+  __shared__ float key[MAX_L];
+  __shared__ int idx[MAX_L];
+  __shared__ double prefix_last, prefix_k, prefix_R;
+  __shared__ int sk, sR, sstatus;
+  __shared__ float sc;
+  const int tid = threadIdx.x;
+  int Lp2 = 1;
+  while (Lp2 < L) Lp2 <<= 1;
+  for (int i = tid; i < Lp2; i += 1024) {
+    key[i] = i < L ? nrm[i] : -1.0f;  // padding sorts last
+    idx[i] = i;
+  }
+  __syncthreads();
+  // bitonic sort, descending by key, ascending index on ties
+  for (int size = 2; size <= Lp2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < Lp2; i += 1024) {
+        const int jx = i ^ stride;
+        if (jx > i) {
+          const bool desc = (i & size) == 0;
+          const float ki = key[i], kj = key[jx];
+          const int ii = idx[i], ij = idx[jx];
+          const bool i_first = (ki > kj) || (ki == kj && ii < ij);  // i should precede j
+          if (desc ? !i_first : i_first) {
+            key[i] = kj;
+            key[jx] = ki;
+            idx[i] = ij;
+            idx[jx] = ii;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < L; i += 1024) sigma_out[i] = key[i];
+
+  if (tid == 0) {
+    int status = 0;
+    if (*bad) status = 6;            // non-finite statistics
+    else if (!*converged) status = 7;  // no convergence
+    // ordered float64 prefix of sigma^2
+    double run = 0.0;
+    for (int i = 0; i < L; ++i) {
+      const double sgm = (double)key[i];
+      run += sgm * sgm;
+    }
+    const double E = run;
+    int k = 0;
+    double Sk = 0.0, SR = 0.0;
+    if (status == 0 && !(E > 0.0)) status = (E == 0.0) ? 5 : 6;
+    if (status == 0) {
+      const double thr = (double)eps * E;
+      run = 0.0;
+      for (int i = 0; i < L; ++i) {
+        const double sgm = (double)key[i];
+        run += sgm * sgm;
+        if (run >= thr) {
+          k = i + 1;
+          Sk = run;
+          break;
+        }
+      }
+      if (k == 0) {  // rounding made the total fall short of eps*E: only possible at eps == 1
+        k = L;
+        Sk = E;
+      }
+    }
+    int R = k + p < L ? k + p : L;
+    if (status == 0 && R > R_max) status = 4;
+    float c = 1.0f;
+    if (status == 0) {
+      run = 0.0;
+      for (int i = 0; i < R; ++i) {
+        const double sgm = (double)key[i];
+        run += sgm * sgm;
+      }
+      SR = run;
+      if (comp == 0) c = (float)(1.0 / sqrt(SR));
+      else if (comp == 2) c = (float)sqrt(E / SR);
+    }
+    prefix_last = E;
+    prefix_k = Sk;
+    prefix_R = SR;
+    sk = k;
+    sR = R;
+    sc = c;
+    sstatus = status;
+  }
+  __syncthreads();
+  if (sstatus == 0) {
+    // P[r][l] = c * W[idx_r][l] / sigma_r, sign fixed so the largest |entry| is positive
+    const int R = sR;
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int r = wave; r < R; r += 16) {
+      const int colr = idx[r];
+      // a direction with no energy carries no eigenvector information: its row stays zero
+      const float inv = key[r] > 0.0f ? 1.0f / key[r] : 0.0f;
+      float best = -1.0f;
+      int bl = 0x7fffffff;
+      float bv = 0.0f;
+      for (int l = lane; l < L; l += 64) {
+        const float v = W[(size_t)colr * ldw + l];
+        const float a = fabsf(v);
+        if (a > best || (a == best && l < bl)) {
+          best = a;
+          bl = l;
+          bv = v;
+        }
+      }
+      for (int off = 32; off > 0; off >>= 1) {
+        const float ob = __shfl_xor(best, off);
+        const int ol = __shfl_xor(bl, off);
+        const float ov = __shfl_xor(bv, off);
+        if (ob > best || (ob == best && ol < bl)) {
+          best = ob;
+          bl = ol;
+          bv = ov;
+        }
+      }
+      const float sgn = bv < 0.0f ? -1.0f : 1.0f;
+      const float scale = sgn * sc * inv;
+      for (int l = lane; l < L; l += 64) P32[(size_t)r * L + l] = scale * W[(size_t)colr * ldw + l];
+    }
+  }
+  if (tid == 0) {
+    info[INFO_STATUS] = sstatus;
+    info[INFO_K] = sk;
+    info[INFO_R] = sR;
+    info[INFO_C] = __float_as_int(sc);
+    const double kept = prefix_last > 0.0 ? prefix_R / prefix_last : 0.0;
+    const double keptk = prefix_last > 0.0 ? prefix_k / prefix_last : 0.0;
+    *reinterpret_cast<double*>(info + INFO_KEPT) = kept;
+    *reinterpret_cast<double*>(info + INFO_KEPTK) = keptk;
+  }
+}
+
+
+// ---------------------------------------------------------------------------- driver
+
+hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv_ng, int L, int max_sweeps,
+                   bool warm, void* work, const EigOut& out, int host_flags[EIG_HOST_FLAGS], hipStream_t st) {
+  if (L > JAC_MAX_LDW) return hipErrorInvalidValue;
+  const EigLayout e = eig_layout(L);
+  const EigBufs b = eig_bufs(work, e);
+  int* flags = b.flags;
+  double* scale = (double*)(flags + F_SCALE);
+  hipError_t err;
+  if ((err = launch_zero(flags, EIG_FLAGS_BYTES + e.verbytes, st)) != hipSuccess) return err;
+  const double* S[2] = {SX, SG};
+  const double inv[2] = {inv_nx, inv_ng};
+  for (int s = 0; s < 2; ++s) {
+    if (warm) {
+      hipLaunchKernelGGL(jacobi_prep_kernel, dim3(e.ncols), dim3(256), 0, st, S[s], inv[s], L, e.ldw, b.Wtmp,
+                         flags + F_BAD + s);
+      hipLaunchKernelGGL(warm_gemm_kernel, dim3((e.ldw + 63) / 64, (e.ncols + 63) / 64), dim3(256), 0, st, b.Wtmp,
+                         b.V[s], L, e.ldw, e.ncols, b.W[s]);
+    } else {
+      hipLaunchKernelGGL(jacobi_prep_kernel, dim3(e.ncols), dim3(256), 0, st, S[s], inv[s], L, e.ldw, b.W[s],
+                         flags + F_BAD + s);
+      hipLaunchKernelGGL(identity_kernel, dim3(e.ncols), dim3(256), 0, st, b.V[s], e.ldw);
+    }
+    hipLaunchKernelGGL(colnorm_kernel, dim3(L), dim3(64), 0, st, b.W[s], e.ldw, L, b.nrm[s]);
+    hipLaunchKernelGGL(frob_kernel, dim3(1), dim3(256), 0, st, b.nrm[s], L, scale + s);
+    hipLaunchKernelGGL(alive_kernel, dim3(1), dim3(1024), 0, st, b.nrm[s], scale + s, L, e.ncols, b.cols[s],
+                       flags + F_NALIVE + s);
+  }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
+  JacobiArgs ja;
+  ja.W[0] = b.W[0];
+  ja.W[1] = b.W[1];
+  ja.V[0] = b.V[0];
+  ja.V[1] = b.V[1];
+  ja.scale = scale;
+  ja.offmax = (unsigned*)(flags + F_OFFMAX);
+  ja.out = flags + F_SWEEPS;
+  ja.barrier = flags + F_BARRIER;
+  ja.abort = flags + F_ABORT;
+  ja.version = b.version;
+  ja.cols[0] = b.cols[0];
+  ja.cols[1] = b.cols[1];
+  ja.n_alive = flags + F_NALIVE;
+  ja.L = L;
+  ja.ldw = e.ldw;
+  ja.nb = e.nb;
+  ja.max_sweeps = max_sweeps;
+  // fp32 Gram entries carry a relative rounding error of about sqrt(L) * 2^-24
+  ja.tol = fmaxf(1e-6f, 8.0f * sqrtf((float)e.ldw) * 5.96e-8f);
+  ja.rot_tol = 0.25f * ja.tol;
+  void* kargs[] = {&ja};
+  const size_t dyn = (size_t)16 * e.ldw * sizeof(float);
+  err = hipLaunchCooperativeKernel((const void*)jacobi_kernel, dim3(e.nb), dim3(256), kargs, dyn, st);
+  if (err != hipSuccess) return err;
+
+  float* P[2] = {out.P32, out.Q32};
+  float* sig[2] = {out.sigma_x, out.sigma_g};
+  int* info[2] = {out.info_x, out.info_g};
+  for (int s = 0; s < 2; ++s) {
+    hipLaunchKernelGGL(colnorm_kernel, dim3(L), dim3(64), 0, st, b.W[s], e.ldw, L, b.nrm[s]);
+    hipLaunchKernelGGL(truncate_build_kernel, dim3(1), dim3(1024), 0, st, b.W[s], e.ldw, L, b.nrm[s], out.eps, out.p,
+                       out.comp, out.R_max, flags + F_BAD + s, flags + F_CONV + s, P[s], sig[s], info[s]);
+  }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = hipMemcpyAsync(host_flags, flags, EIG_HOST_FLAGS * sizeof(int), hipMemcpyDeviceToHost, st)) != hipSuccess)
+    return err;
+  if ((err = hipStreamSynchronize(st)) != hipSuccess) return err;
+  if (host_flags[F_ABORT]) return hipErrorLaunchTimeOut;  // a bounded wait gave up
+  return hipSuccess;
+}
+
+int eig_max_L() { return JAC_MAX_LDW; }
+
+}  // namespace instant

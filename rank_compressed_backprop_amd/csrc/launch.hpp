@@ -36,8 +36,9 @@ int syrk_tiles(int L);
 // by blocked one-sided Jacobi, then truncation, compensation and the float32
 // projections P32 [Rx][L] / Q32 [Ry][L], the descending spectra and the per-side
 // device info blocks (int32 slots: status, k, R, c bits, kept (f64), kept_k (f64)).
-// Synchronous: reads the convergence flags once per sweep. host_flags receives
-// [offmax x2, active x2, sweeps x2, converged x2, nonfinite x2].
+// warm: start from the rotation accumulated by the previous call (kept in `work`).
+// Synchronous (one stream synchronisation at the end). host_flags receives the
+// first EIG_HOST_FLAGS int32 slots of the flags block (see kernels_eig.hip).
 struct EigOut {
   float eps;
   int p, comp, R_max;
@@ -49,9 +50,12 @@ struct EigOut {
   int* info_g;
 };
 constexpr int INFO_WORDS = 8;
+constexpr int EIG_HOST_FLAGS = 20;
+constexpr int EIGF_SWEEPS = 6, EIGF_CONV = 8, EIGF_BAD = 10, EIGF_NALIVE = 18;
 size_t eig_workspace_bytes(int L);
+int eig_max_L();
 hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv_ng, int L, int max_sweeps,
-                   void* work, const EigOut& out, int host_flags[10], hipStream_t st);
+                   bool warm, void* work, const EigOut& out, int host_flags[EIG_HOST_FLAGS], hipStream_t st);
 
 // I/O-dtype copies of the active projections: PQ [2*R_max][ldL] (rows [0,Rx) = P,
 // [Rx,Rx+Ry) = Q, zero elsewhere) and Qt [L][ldQt] (zero beyond Ry).

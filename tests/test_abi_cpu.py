@@ -44,7 +44,7 @@ def test_workspace_bytes_validates_config():
     n = rcb.instant_workspace_bytes(good)
     assert n > 2 * 512 * 512 * 8  # at least the two float64 statistic sums
     bad = [
-        dict(L=0), dict(L=5000), dict(Cx=12), dict(Cy=0), dict(B_max=0), dict(R_max=65),
+        dict(L=0), dict(L=2049), dict(Cx=12), dict(Cy=0), dict(B_max=0), dict(R_max=65),
         dict(eps=0.0), dict(eps=1.5), dict(dtype=7), dict(comp=5), dict(max_sweeps=0), dict(p=-1),
     ]
     for change in bad:
