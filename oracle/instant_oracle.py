@@ -33,7 +33,7 @@ import numpy as np
 __all__ = [
     "OK", "E_ARG", "E_SHAPE", "E_STATE", "E_RANK", "E_ENERGY", "E_NONFINITE", "E_NOCONV",
     "COMP_PAPER", "COMP_NONE", "COMP_RATIO",
-    "Accumulator", "spectrum", "truncate", "compensation", "build_projection",
+    "Accumulator", "autocorr_entries", "spectrum", "truncate", "compensation", "build_projection",
     "calibrate_side", "calibrate", "compress", "backward", "dense_projector_backward",
     "exact_backward", "flops_lowrank_formula", "flops_vanilla_formula", "FlopCounter",
     "canonical_signs", "eps_as_f32",
@@ -73,6 +73,22 @@ class Accumulator:
     def mean(self) -> np.ndarray:
         """C = E[t t^T], the mean over the samples seen."""
         return self.S / self.n
+
+
+def autocorr_entries(batches, rows, cols) -> np.ndarray:
+    """Selected entries C[rows[m], cols[m]] of C = E[t t^T] ([KD1]), each computed from
+    its definition: the mean over samples of the channel dot product of two token rows.
+    For sizes where the full L x L statistic is too large for the oracle."""
+    rows = np.asarray(rows)
+    cols = np.asarray(cols)
+    acc = np.zeros(rows.shape[0], dtype=np.float64)
+    n = 0
+    for t in batches:
+        t = np.asarray(t, dtype=np.float64)
+        for b in range(t.shape[0]):
+            acc += np.einsum("mc,mc->m", t[b, rows, :], t[b, cols, :])
+        n += t.shape[0]
+    return acc / n
 
 
 # ----------------------------------------------------------------------------- [KD1]/[KD2] decomposition

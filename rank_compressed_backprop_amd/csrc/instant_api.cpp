@@ -117,7 +117,10 @@ inline instant_status hip_ok(hipError_t e) { return e == hipSuccess ? INSTANT_OK
 instant_status accumulate(instant_layer* h, const void* t, int B, int C, double* Sacc, hipStream_t st) {
   const int steps = (C + (h->bf16 ? 32 : 16) - 1) / (h->bf16 ? 32 : 16);
   const long total = (long)B * steps;
-  int nsplit = (int)std::min<long>(syrk_split_cap(h->cfg.L), std::max<long>(1, total / 4));
+  // every wave of a slice gets at least U = 4 steps; a multiple of 8 slices when there
+  // are that many (one XCD per slice)
+  int nsplit = (int)std::min<long>(syrk_split_cap(h->cfg.L), std::max<long>(1, total / 16));
+  if (nsplit >= 16) nsplit -= nsplit % 8;
   hipError_t e = launch_syrk(h->bf16, t, B, h->cfg.L, C, nsplit, h->part(), st);
   if (e != hipSuccess) return INSTANT_E_HIP;
   return hip_ok(launch_syrk_reduce(h->part(), nsplit, h->cfg.L, Sacc, st));
@@ -274,10 +277,15 @@ INSTANT_API instant_status instant_backward(instant_layer* h, const void* xhat, 
   hipError_t e = launch_proj(h->bf16, h->PQ(a), h->lay.ldL, Rx + Ry, Rx, gy, B, L, Cy, Pgy, Qgy, st);
   // g_w = sum_b (P gy_b)^T x_hat_b: M = Cy, N = Cx, K = B * Rx
   if (e == hipSuccess) e = launch_gemm(h->bf16, true, Pgy, Cy, 0, xhat, Cx, 0, gw, Cx, 0, 1, Cy, Cx, B * Rx, st);
-  // g_hat_x = (Q gy) w: M = B * Ry, N = Cx, K = Cy
-  if (e == hipSuccess) e = launch_gemm(h->bf16, false, Qgy, Cy, 0, w, Cx, 0, gxh, Cx, 0, 1, B * Ry, Cx, Cy, st);
-  // g_x_b = Q^T g_hat_x_b
-  if (e == hipSuccess) e = launch_expand(h->bf16, h->Qt(a), LD_QT, gxh, B, Ry, L, Cx, gx, st);
+  if (gx_fused_applies(h->bf16, B, Cx, Cy)) {
+    // g_x_b = Q^T ((Q gy_b) w) in one kernel, w resident in L2
+    if (e == hipSuccess) e = launch_gx_fused(h->bf16, Qgy, w, h->Qt(a), LD_QT, B, Ry, L, Cy, Cx, gx, st);
+  } else {
+    // g_hat_x = (Q gy) w: M = B * Ry, N = Cx, K = Cy
+    if (e == hipSuccess) e = launch_gemm(h->bf16, false, Qgy, Cy, 0, w, Cx, 0, gxh, Cx, 0, 1, B * Ry, Cx, Cy, st);
+    // g_x_b = Q^T g_hat_x_b
+    if (e == hipSuccess) e = launch_expand(h->bf16, h->Qt(a), LD_QT, gxh, B, Ry, L, Cx, gx, st);
+  }
   return hip_ok(e);
 }
 

@@ -38,9 +38,21 @@ __global__ __launch_bounds__(256) void syrk_kernel(const T* __restrict__ X, int 
   const int lane = threadIdx.x & (WAVE - 1);
   const int wave = threadIdx.x / WAVE;
   const int Tn = (L + ST - 1) / ST;
+  const int ntiles = Tn * (Tn + 1) / 2;
+  // Workgroups are dealt to the 8 XCDs round-robin by linear id. When there are at least
+  // 8 slices, give all tiles of a slice to one XCD so each sample is fetched into one L2.
+  int tile, s;
+  const int lin = blockIdx.x;
+  if (nsplit % 8 == 0) {
+    const int xcd = lin % 8, k = lin / 8;
+    s = xcd + 8 * (k / ntiles);
+    tile = k % ntiles;
+  } else {
+    s = lin / ntiles;
+    tile = lin % ntiles;
+  }
   int ti, tj;
-  upper_tile(blockIdx.x, Tn, ti, tj);
-  const int s = blockIdx.y;
+  upper_tile(tile, Tn, ti, tj);
   const int steps_c = (C + mm::KSTEP - 1) / mm::KSTEP;
   const long total = (long)B * steps_c;
   const long beg = total * s / nsplit;
@@ -53,30 +65,38 @@ __global__ __launch_bounds__(256) void syrk_kernel(const T* __restrict__ X, int 
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc[t][u] = zero4();
 
-  for (long q = beg + wave; q < end; q += NW) {
-    const int b = (int)(q / steps_c);
-    const int kk = (int)(q % steps_c) * mm::KSTEP + kl;
-    const T* __restrict__ Xb = X + (size_t)b * L * C;
-    const bool kok = kk < C;
-    frag a[4], bb[4];
+  constexpr int U = 4;  // k-steps whose loads are in flight together
+  for (long q0 = beg + wave; q0 < end; q0 += NW * U) {
+    frag a[U][4], bb[U][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int r = ti * ST + 16 * t + (lane & 15);
-      a[t] = load_frag<T>(Xb + (size_t)r * C + kk, kok && r < L);
+    for (int u = 0; u < U; ++u) {
+      const long q = q0 + u * NW;
+      const bool qok = q < end;
+      const int b = qok ? (int)(q / steps_c) : 0;
+      const int kk = (int)(q % steps_c) * mm::KSTEP + kl;
+      const T* __restrict__ Xb = X + (size_t)b * L * C;
+      const bool kok = qok && kk < C;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int r = ti * ST + 16 * t + (lane & 15);
+        a[u][t] = load_frag<T>(Xb + (size_t)r * C + kk, kok && r < L);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int r = tj * ST + 16 * t + (lane & 15);
+        bb[u][t] = load_frag<T>(Xb + (size_t)r * C + kk, kok && r < L);
+      }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = tj * ST + 16 * u + (lane & 15);
-      bb[u] = load_frag<T>(Xb + (size_t)r * C + kk, kok && r < L);
-    }
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[t][u] = mm::mma(a[t], bb[u], acc[t][u]);
+        for (int v = 0; v < 4; ++v) acc[t][v] = mm::mma(a[u][t], bb[u][v], acc[t][v]);
   }
 
   __shared__ float red[NW][4][4][WAVE];
-  float* __restrict__ out = part + ((size_t)s * gridDim.x + blockIdx.x) * (ST * ST);
+  float* __restrict__ out = part + ((size_t)s * ntiles + tile) * (ST * ST);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
 #pragma unroll
@@ -111,14 +131,26 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
   const int i = ti * ST + e / ST;
   const int j = tj * ST + e % ST;
   if (i >= L || j >= L) return;
+  // independent loads, summed in split order
+  const float* __restrict__ pp = part + (size_t)tile * (ST * ST) + e;
+  const size_t stride = (size_t)ntiles * (ST * ST);
   double acc = 0.0;
-  for (int s = 0; s < nsplit; ++s) acc += (double)part[((size_t)s * ntiles + tile) * (ST * ST) + e];
+  int s = 0;
+  for (; s + 4 <= nsplit; s += 4) {
+    const float v0 = pp[(s + 0) * stride], v1 = pp[(s + 1) * stride];
+    const float v2 = pp[(s + 2) * stride], v3 = pp[(s + 3) * stride];
+    acc += (double)v0;
+    acc += (double)v1;
+    acc += (double)v2;
+    acc += (double)v3;
+  }
+  for (; s < nsplit; ++s) acc += (double)pp[s * stride];
   S[(size_t)i * L + j] += acc;
 }
 
 template <class T>
 static hipError_t syrk_t(const void* X, int B, int L, int C, int nsplit, float* part, hipStream_t st) {
-  dim3 grid(syrk_tiles(L), nsplit);
+  dim3 grid(syrk_tiles(L) * nsplit);
   hipLaunchKernelGGL(syrk_kernel<T>, grid, dim3(256), 0, st, (const T*)X, B, L, C, nsplit, part);
   return hipGetLastError();
 }

@@ -133,45 +133,52 @@ __global__ __launch_bounds__(256) void identity_kernel(double* __restrict__ V, i
   for (int r = threadIdx.x; r < ldw; r += 256) V[(size_t)c * ldw + r] = (r == c) ? 1.0 : 0.0;
 }
 
-// Warm start: W[c][r] = sum_k C[r][k] V[c][k] with C symmetric (float32, column-major in
-// Ct), V float64, float64 accumulation. 64x64 output tiles, k in chunks of 16 through LDS.
-__global__ __launch_bounds__(256) void warm_gemm_kernel(const float* __restrict__ Ct, const double* __restrict__ V,
-                                                        int L, int ldw, int ncols, float* __restrict__ W) {
-  __shared__ double Cs[16][65];
-  __shared__ double Vs[16][65];
-  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  const int tr = threadIdx.x & 15, tc = threadIdx.x >> 4;
-  double acc[4][4] = {};
-  for (int k0 = 0; k0 < L; k0 += 16) {
-    for (int e = threadIdx.x; e < 16 * 64; e += 256) {
-      const int kk = e >> 6, rr = e & 63;
-      const int k = k0 + kk;
-      Cs[kk][rr] = (k < L && r0 + rr < ldw) ? (double)Ct[(size_t)k * ldw + r0 + rr] : 0.0;
-      const int cc = e >> 4, k2 = e & 15;
-      Vs[k2][cc] = (k0 + k2 < L && c0 + cc < ncols) ? V[(size_t)(c0 + cc) * ldw + k0 + k2] : 0.0;
+// Warm start: W = C V on the float32 matrix cores, C symmetric (float32, column-major in
+// Ct), V read from its float64 master (column-major). Output tile: 16*4 columns of W x 128
+// rows; D[c][r] = sum_k V[k][c] C[r][k], A = V^T (k contiguous), B = C (r contiguous).
+// Rounding V to float32 here only perturbs W at float32 resolution; the accumulated
+// rotation itself stays float64.
+__global__ __launch_bounds__(64) void warm_gemm_kernel(const float* __restrict__ Ct, const double* __restrict__ V,
+                                                       int L, int ldw, int ncols, float* __restrict__ W) {
+  typedef MM<float> mm;
+  const int lane = threadIdx.x;
+  const int rcol = blockIdx.x * 128 + 8 * (lane & 15);  // W row (B operand column)
+  const int c0 = blockIdx.y * 64;                       // W column block
+  const bool r_ok = rcol < ldw;
+  const int kl = mm::G * (lane >> 4);
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[t][j] = zero4();
+  for (int k0 = 0; k0 < L; k0 += mm::KSTEP) {
+    mm::frag bf[8];
+    load_strip_T<float, 8>(Ct, ldw, k0 + kl, L, rcol, r_ok, bf);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c = c0 + 16 * t + (lane & 15);
+      mm::frag af;
+#pragma unroll
+      for (int g = 0; g < mm::G; ++g) {
+        const int k = k0 + kl + g;
+        af[g] = (c < ncols && k < L) ? (float)V[(size_t)c * ldw + k] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[t][j] = mm::mma(af, bf[j], acc[t][j]);
     }
-    __syncthreads();
-#pragma unroll 4
-    for (int kk = 0; kk < 16; ++kk) {
-      double cr[4], vc[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) cr[i] = Cs[kk][tr + 16 * i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vc[j] = Vs[kk][tc + 16 * j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(cr[i], vc[j], acc[i][j]);
-    }
-    __syncthreads();
   }
+  if (!r_ok) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = r0 + tr + 16 * i;
-      const int c = c0 + tc + 16 * j;
-      if (r < ldw && c < ncols) W[(size_t)c * ldw + r] = (float)acc[i][j];
+    for (int v = 0; v < 4; ++v) {
+      const int c = c0 + 16 * t + 4 * (lane >> 4) + v;
+      if (c < ncols) {
+        float o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = acc[t][j][v];
+        store_row<float, 8>(W + (size_t)c * ldw + rcol, o);
+      }
     }
 }
 
@@ -210,26 +217,41 @@ __global__ __launch_bounds__(1024) void alive_kernel(const float* __restrict__ n
                                                      int L, int ncols, int* __restrict__ cols,
                                                      int* __restrict__ n_alive) {
   __shared__ int flag[2048];
-  __shared__ int pos[2048];
+  __shared__ int sum[1024];
   const double floor_g = NOISE_REL * *scale;
-  for (int c = threadIdx.x; c < ncols; c += 1024) {
-    const double n = c < L ? (double)nrm[c] : 0.0;
-    flag[c] = (c < L && n * n > floor_g) ? 1 : 0;
+  const int tid = threadIdx.x;
+  // two columns per thread (ncols <= 2048)
+  int f[2], own = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = 2 * tid + h;
+    const double n = (c < L) ? (double)nrm[c] : 0.0;
+    f[h] = (c < ncols && c < L && n * n > floor_g) ? 1 : 0;
+    if (c < ncols) flag[c] = f[h];
+    own += f[h];
   }
+  sum[tid] = own;
   __syncthreads();
-  if (threadIdx.x == 0) {  // ordered scan (ncols <= 2048)
-    int a = 0;
-    for (int c = 0; c < ncols; ++c) {
-      pos[c] = a;
-      a += flag[c];
-    }
-    *n_alive = a;
-    int d = a;
-    for (int c = 0; c < ncols; ++c) {
-      if (flag[c]) cols[pos[c]] = c;
-      else cols[d++] = c;
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan of the per-thread counts
+    const int v = tid >= off ? sum[tid - off] : 0;
+    __syncthreads();
+    sum[tid] += v;
+    __syncthreads();
+  }
+  const int total = sum[1023];
+  const int before = sum[tid] - own;              // alive columns before this thread's pair
+  const int c0 = 2 * tid;
+  int apos = before;                              // position among the alive columns
+  int dpos = total + (c0 - before);               // position among the others
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = c0 + h;
+    if (c < ncols) {
+      if (flag[c]) cols[apos++] = c;
+      else cols[dpos++] = c;
     }
   }
+  if (tid == 0) *n_alive = total;
 }
 
 // ---------------------------------------------------------------------------- Jacobi
@@ -699,7 +721,7 @@ hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv
     if (warm) {
       hipLaunchKernelGGL(jacobi_prep_kernel, dim3(e.ncols), dim3(256), 0, st, S[s], inv[s], L, e.ldw, b.Wtmp,
                          flags + F_BAD + s);
-      hipLaunchKernelGGL(warm_gemm_kernel, dim3((e.ldw + 63) / 64, (e.ncols + 63) / 64), dim3(256), 0, st, b.Wtmp,
+      hipLaunchKernelGGL(warm_gemm_kernel, dim3((e.ldw + 127) / 128, (e.ncols + 63) / 64), dim3(64), 0, st, b.Wtmp,
                          b.V[s], L, e.ldw, e.ncols, b.W[s]);
     } else {
       hipLaunchKernelGGL(jacobi_prep_kernel, dim3(e.ncols), dim3(256), 0, st, S[s], inv[s], L, e.ldw, b.W[s],

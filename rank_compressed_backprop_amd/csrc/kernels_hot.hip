@@ -16,9 +16,10 @@ namespace instant {
 // Out[b][m][c] = sum_{l < L} A[m][l] X[b][l][c] for m < M, c < C.
 // A is [>= M rows][ldA] with zero columns from L up to ldA (ldA a multiple of KSTEP).
 // Rows m < M0 go to out0 [B][M0][C]; rows M0 <= m < M go to out1 [B][M - M0][C].
-// Grid: (ceil(C / 128), B). Each of the NW waves of a block takes every NW-th k-step
-// of the same 128-column strip; the partial tiles are summed through LDS in wave order.
-template <class T, int MT, int NW, int U>
+// Grid: (ceil(C / (16 * SW)), B). A lane owns SW adjacent columns; the NW waves of a
+// block take every NW-th k-step of the same column strip and issue the loads of U
+// steps before any product; the partial tiles are summed through LDS in wave order.
+template <class T, int MT, int NW, int U, int SW>
 __global__ __launch_bounds__(NW * WAVE) void proj_kernel(const T* __restrict__ A, int ldA, int M, int M0,
                                                          const T* __restrict__ X, int L, int C,
                                                          T* __restrict__ out0, T* __restrict__ out1) {
@@ -27,47 +28,46 @@ __global__ __launch_bounds__(NW * WAVE) void proj_kernel(const T* __restrict__ A
   const int lane = threadIdx.x & (WAVE - 1);
   const int wave = threadIdx.x / WAVE;
   const int b = blockIdx.y;
-  const int col = blockIdx.x * 128 + 8 * (lane & 15);
+  const int col = blockIdx.x * (16 * SW) + SW * (lane & 15);
   const bool col_ok = col < C;
   const T* __restrict__ Xb = X + (size_t)b * L * C;
   const int arow = lane & 15;
   const int kl = mm::G * (lane >> 4);
 
-  f32x4 acc[MT][8];
+  f32x4 acc[MT][SW];
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[t][j] = zero4();
+    for (int j = 0; j < SW; ++j) acc[t][j] = zero4();
 
   const int nsteps = (L + mm::KSTEP - 1) / mm::KSTEP;
   for (int s0 = wave; s0 < nsteps; s0 += NW * U) {
-    frag bf[U][8];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k0 = (s0 + u * NW) * mm::KSTEP + kl;
-      load_strip_T<T, 8>(Xb, C, k0, L, col, col_ok, bf[u]);
-    }
+    frag bf[U][SW];
+    frag af[U][MT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = s0 + u * NW;
-      if (s < nsteps) {
-        const int k0 = s * mm::KSTEP + kl;
+      const int k0 = s * mm::KSTEP + kl;
+      load_strip_T<T, SW>(Xb, C, k0, L, col, col_ok, bf[u]);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const int m = 16 * t + arow;
-          frag af = load_frag<T>(A + (size_t)m * ldA + k0, m < M);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[t][j] = mm::mma(af, bf[u][j], acc[t][j]);
-        }
+      for (int t = 0; t < MT; ++t) {
+        const int m = 16 * t + arow;
+        af[u][t] = load_frag<T>(A + (size_t)m * ldA + k0, m < M && s < nsteps);
       }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int j = 0; j < SW; ++j) acc[t][j] = mm::mma(af[u][t], bf[u][j], acc[t][j]);
   }
 
   const int Mb = M - M0;
-  auto store = [&](int m, const float v[8]) {
+  auto store = [&](int m, const float v[SW]) {
     if (m >= M || !col_ok) return;
     T* dst = (m < M0) ? out0 + ((size_t)b * M0 + m) * C + col : out1 + ((size_t)b * Mb + (m - M0)) * C + col;
-    store_row<T, 8>(dst, v);
+    store_row<T, SW>(dst, v);
   };
 
   if constexpr (NW == 1) {
@@ -75,24 +75,24 @@ __global__ __launch_bounds__(NW * WAVE) void proj_kernel(const T* __restrict__ A
     for (int t = 0; t < MT; ++t)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        float o[8];
+        float o[SW];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = acc[t][j][v];
+        for (int j = 0; j < SW; ++j) o[j] = acc[t][j][v];
         store(16 * t + 4 * (lane >> 4) + v, o);
       }
   } else {
-    __shared__ float red[NW][8][4][WAVE];
+    __shared__ float red[NW][SW][4][WAVE];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < SW; ++j)
 #pragma unroll
         for (int v = 0; v < 4; ++v) red[wave][j][v][lane] = acc[t][j][v];
       __syncthreads();
       for (int v = wave; v < 4; v += NW) {
-        float o[8];
+        float o[SW];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < SW; ++j) {
           float sum = red[0][j][v][lane];
 #pragma unroll
           for (int w = 1; w < NW; ++w) sum += red[w][j][v][lane];
@@ -111,8 +111,9 @@ __global__ __launch_bounds__(NW * WAVE) void proj_kernel(const T* __restrict__ A
 // A_TRANS = true : A is [K][lda] (m contiguous); a lane reads 4 adjacent rows as
 //                  virtual tiles, the wave covers 64 rows (MT must be 4).
 // B is [K][ldb] (n contiguous); the wave covers 128 columns.
-// Grid: (ceil(N / 128), ceil(M / rows per wave), batch); the NW waves of a block split K.
-template <class T, bool A_TRANS, int MT, int NW>
+// Grid: (ceil(N / 128), ceil(M / rows per wave), batch); the NW waves of a block split K,
+// each issuing the loads of U steps before any product.
+template <class T, bool A_TRANS, int MT, int NW, int U>
 __global__ __launch_bounds__(NW * WAVE) void gemm_kernel(const T* __restrict__ A, int lda, size_t strideA,
                                                          const T* __restrict__ Bm, int ldb, size_t strideB,
                                                          T* __restrict__ Cm, int ldc, size_t strideC,
@@ -138,34 +139,40 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_kernel(const T* __restrict__ A
     for (int j = 0; j < 8; ++j) acc[t][j] = zero4();
 
   const int nsteps = (K + mm::KSTEP - 1) / mm::KSTEP;
-  for (int s = wave; s < nsteps; s += NW) {
-    const int k0 = s * mm::KSTEP + kl;
-    frag bf[8];
-    load_strip_T<T, 8>(Bm, ldb, k0, K, col, col_ok, bf);
-    frag af[MT];
-    if constexpr (A_TRANS) {
-      static_assert(MT == 4, "transposed A uses 4-wide strips");
-      const int acol = m0 + 4 * (lane & 15);
-      load_strip_T<T, 4>(A, lda, k0, K, acol, acol < M, af);
-    } else {
+  for (int s0 = wave; s0 < nsteps; s0 += NW * U) {
+    frag bf[U][8];
+    frag af[U][MT];
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const int m = m0 + 16 * t + (lane & 15);
-        // the k tail of a direct operand is masked element-wise only when K is ragged
-        if (m < M && k0 + mm::G <= K) {
-          af[t] = load_frag<T>(A + (size_t)m * lda + k0, true);
-        } else {
-          af[t] = zero_frag<T>();
-          if (m < M)
-            for (int g = 0; g < mm::G; ++g)
-              if (k0 + g < K) af[t][g] = A[(size_t)m * lda + k0 + g];
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * NW;
+      const int k0 = s * mm::KSTEP + kl;
+      load_strip_T<T, 8>(Bm, ldb, k0, K, col, col_ok, bf[u]);
+      if constexpr (A_TRANS) {
+        static_assert(MT == 4, "transposed A uses 4-wide strips");
+        const int acol = m0 + 4 * (lane & 15);
+        load_strip_T<T, 4>(A, lda, k0, K, acol, acol < M, af[u]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const int m = m0 + 16 * t + (lane & 15);
+          if (m < M && k0 + mm::G <= K) {
+            af[u][t] = load_frag<T>(A + (size_t)m * lda + k0, true);
+          } else {
+            // ragged k tail of a direct operand: element-wise, zero beyond K
+            af[u][t] = zero_frag<T>();
+            if (m < M)
+              for (int g = 0; g < mm::G; ++g)
+                if (k0 + g < K) af[u][t][g] = A[(size_t)m * lda + k0 + g];
+          }
         }
       }
     }
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[t][j] = mm::mma(af[t], bf[j], acc[t][j]);
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[t][j] = mm::mma(af[u][t], bf[u][j], acc[t][j]);
   }
 
   auto row_of = [&](int t, int v) {
@@ -235,6 +242,13 @@ __global__ __launch_bounds__(NW * WAVE) void expand_kernel(const T* __restrict__
   for (int ks = 0; ks < KS; ++ks) load_strip_T<T, 8>(Bb, C, ks * mm::KSTEP + kl, R, col, col_ok, bf[ks]);
 
   const int tile0 = (blockIdx.z * NW + wave) * MPW;
+  frag af[MPW][KS];
+#pragma unroll
+  for (int i = 0; i < MPW; ++i) {
+    const int la = 16 * (tile0 + i) + (lane & 15);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) af[i][ks] = load_frag<T>(At + (size_t)la * ldA + ks * mm::KSTEP + kl, la < L);
+  }
 #pragma unroll
   for (int i = 0; i < MPW; ++i) {
     const int l0 = 16 * (tile0 + i);
@@ -242,13 +256,10 @@ __global__ __launch_bounds__(NW * WAVE) void expand_kernel(const T* __restrict__
     f32x4 acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = zero4();
-    const int la = l0 + (lane & 15);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      frag af = load_frag<T>(At + (size_t)la * ldA + ks * mm::KSTEP + kl, la < L);
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = mm::mma(af, bf[ks][j], acc[j]);
-    }
+      for (int j = 0; j < 8; ++j) acc[j] = mm::mma(af[i][ks], bf[ks][j], acc[j]);
     if (col_ok) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -264,17 +275,150 @@ __global__ __launch_bounds__(NW * WAVE) void expand_kernel(const T* __restrict__
   }
 }
 
+// ----------------------------------------------------------------------------- fused g_x
+// For layers whose weight stays resident in L2: block (strip, b) first forms
+// g_hat_x_b[:, strip] = Qgy_b (Ry x Cy) . w[:, strip] (Cy x 128) on the matrix cores
+// (the NW waves split Cy, LDS sums them), keeps it in LDS in the I/O dtype, and then
+// expands g_x_b[:, strip] = Q^T g_hat_x_b[:, strip] over all L tokens.
+// Grid: (ceil(Cx / 128), B).
+template <class T, int MTA, int KS, int NW>
+__global__ __launch_bounds__(NW * WAVE) void gx_fused_kernel(const T* __restrict__ Qgy, const T* __restrict__ w,
+                                                             const T* __restrict__ At, int ldA, int R, int L,
+                                                             int Cy, int Cx, T* __restrict__ out) {
+  typedef MM<T> mm;
+  typedef typename mm::frag frag;
+  constexpr int U = 2;
+  constexpr int GROWS = KS * MM<T>::KSTEP;  // rows of the LDS operand (zero beyond R)
+  __shared__ float red[NW][8][4][WAVE];
+  __shared__ __attribute__((aligned(16))) T gsm[GROWS][128];
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wave = threadIdx.x / WAVE;
+  const int b = blockIdx.y;
+  const int lc = 8 * (lane & 15);  // column within the strip
+  const int col = blockIdx.x * 128 + lc;
+  const bool col_ok = col < Cx;
+  const int kl = mm::G * (lane >> 4);
+  const T* __restrict__ Ab = Qgy + (size_t)b * R * Cy;
+
+  for (int e = threadIdx.x; e < GROWS * 128; e += NW * WAVE) (&gsm[0][0])[e] = (T)0.0f;
+
+  // phase 1: g_hat_x tile
+  f32x4 acc[MTA][8];
+#pragma unroll
+  for (int t = 0; t < MTA; ++t)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[t][j] = zero4();
+  const int nsteps = (Cy + mm::KSTEP - 1) / mm::KSTEP;
+  for (int s0 = wave; s0 < nsteps; s0 += NW * U) {
+    frag bf[U][8];
+    frag af[U][MTA];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * NW;
+      const int k0 = s * mm::KSTEP + kl;
+      load_strip_T<T, 8>(w, Cx, k0, Cy, col, col_ok, bf[u]);
+#pragma unroll
+      for (int t = 0; t < MTA; ++t) {
+        const int m = 16 * t + (lane & 15);
+        af[u][t] = load_frag<T>(Ab + (size_t)m * Cy + k0, m < R && s < nsteps && k0 + mm::G <= Cy);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < MTA; ++t)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[t][j] = mm::mma(af[u][t], bf[u][j], acc[t][j]);
+  }
+#pragma unroll
+  for (int t = 0; t < MTA; ++t) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wave][j][v][lane] = acc[t][j][v];
+    __syncthreads();
+    for (int v = wave; v < 4; v += NW) {
+      const int r = 16 * t + 4 * (lane >> 4) + v;
+      if (r < R) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float sum = red[0][j][v][lane];
+#pragma unroll
+          for (int ww = 1; ww < NW; ++ww) sum += red[ww][j][v][lane];
+          gsm[r][lc + j] = from_f32<T>(sum);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // phase 2: expand over all tokens; each wave takes every NW-th 16-token tile
+  frag bz[KS][8];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) load_strip_T<T, 8>(&gsm[0][0], 128, ks * mm::KSTEP + kl, R, lc, true, bz[ks]);
+  constexpr int MPW = 4;
+  const int ntl = (L + 15) / 16;
+  for (int tl0 = wave; tl0 < ntl; tl0 += NW * MPW) {
+    frag af[MPW][KS];
+#pragma unroll
+    for (int i = 0; i < MPW; ++i) {
+      const int la = 16 * (tl0 + i * NW) + (lane & 15);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) af[i][ks] = load_frag<T>(At + (size_t)la * ldA + ks * mm::KSTEP + kl, la < L);
+    }
+#pragma unroll
+    for (int i = 0; i < MPW; ++i) {
+      const int l0 = 16 * (tl0 + i * NW);
+      if (l0 >= L) break;
+      f32x4 o4[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o4[j] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o4[j] = mm::mma(af[i][ks], bz[ks][j], o4[j]);
+      if (col_ok) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int l = l0 + 4 * (lane >> 4) + v;
+          if (l < L) {
+            float o[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] = o4[j][v];
+            store_row<T, 8>(out + ((size_t)b * L + l) * Cx + col, o);
+          }
+        }
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------- launchers
 
-template <class T, int MT>
-static hipError_t proj_mt(const void* A, int ldA, int M, int M0, const void* X, int B, int L, int C,
-                          void* out0, void* out1, hipStream_t st) {
-  constexpr int NW = 4;
-  constexpr int U = MT <= 5 ? 2 : 1;  // keeps the widest stacks free of register spills
-  dim3 grid((C + 127) / 128, B);
-  hipLaunchKernelGGL((proj_kernel<T, MT, NW, U>), grid, dim3(NW * WAVE), 0, st, (const T*)A, ldA, M, M0,
+template <class T, int MT, int NW, int SW>
+static hipError_t proj_cfg(const void* A, int ldA, int M, int M0, const void* X, int B, int L, int C, void* out0,
+                           void* out1, hipStream_t st) {
+  constexpr int U = MT <= 2 ? 4 : (MT <= 5 ? 2 : 1);  // loads in flight vs registers
+  dim3 grid((C + 16 * SW - 1) / (16 * SW), B);
+  hipLaunchKernelGGL((proj_kernel<T, MT, NW, U, SW>), grid, dim3(NW * WAVE), 0, st, (const T*)A, ldA, M, M0,
                      (const T*)X, L, C, (T*)out0, (T*)out1);
   return hipGetLastError();
+}
+
+template <class T, int MT>
+static hipError_t proj_mt(const void* A, int ldA, int M, int M0, const void* X, int B, int L, int C, void* out0,
+                          void* out1, hipStream_t st) {
+  const int nsteps = (L + MM<T>::KSTEP - 1) / MM<T>::KSTEP;
+  // narrower strips when 128-column strips would leave compute units idle
+  const bool narrow = (long)((C + 127) / 128) * B < 256 && C > 64;
+  if (nsteps >= 4)
+    return narrow ? proj_cfg<T, MT, 4, 4>(A, ldA, M, M0, X, B, L, C, out0, out1, st)
+                  : proj_cfg<T, MT, 4, 8>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
+  if (nsteps >= 2)
+    return narrow ? proj_cfg<T, MT, 2, 4>(A, ldA, M, M0, X, B, L, C, out0, out1, st)
+                  : proj_cfg<T, MT, 2, 8>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
+  return narrow ? proj_cfg<T, MT, 1, 4>(A, ldA, M, M0, X, B, L, C, out0, out1, st)
+                : proj_cfg<T, MT, 1, 8>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
 }
 
 template <class T>
@@ -299,15 +443,28 @@ hipError_t launch_proj(bool bf16_io, const void* A, int ldA, int M, int M0, cons
                  : proj_t<float>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
 }
 
+template <class T, bool AT, int MT, int NW, int U>
+static hipError_t gemm_cfg(const void* A, int lda, size_t sA, const void* Bm, int ldb, size_t sB, void* Cm, int ldc,
+                           size_t sC, int batch, int M, int N, int K, hipStream_t st) {
+  constexpr int ROWS = AT ? 64 : 16 * MT;
+  dim3 grid((N + 127) / 128, (M + ROWS - 1) / ROWS, batch);
+  hipLaunchKernelGGL((gemm_kernel<T, AT, MT, NW, U>), grid, dim3(NW * WAVE), 0, st, (const T*)A, lda, sA,
+                     (const T*)Bm, ldb, sB, (T*)Cm, ldc, sC, M, N, K);
+  return hipGetLastError();
+}
+
 template <class T, bool AT>
 static hipError_t gemm_t(const void* A, int lda, size_t sA, const void* Bm, int ldb, size_t sB, void* Cm, int ldc,
                          size_t sC, int batch, int M, int N, int K, hipStream_t st) {
-  constexpr int MT = 4;
-  constexpr int NW = 4;
-  dim3 grid((N + 127) / 128, (M + 63) / 64, batch);
-  hipLaunchKernelGGL((gemm_kernel<T, AT, MT, NW>), grid, dim3(NW * WAVE), 0, st, (const T*)A, lda, sA,
-                     (const T*)Bm, ldb, sB, (T*)Cm, ldc, sC, M, N, K);
-  return hipGetLastError();
+  const int nsteps = (K + MM<T>::KSTEP - 1) / MM<T>::KSTEP;
+  if constexpr (AT) {
+    if (nsteps >= 8) return gemm_cfg<T, true, 4, 4, 2>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
+    return gemm_cfg<T, true, 4, 2, 2>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
+  } else {
+    // skinny M: split K over eight waves so each issues few rounds of loads
+    if (nsteps >= 16) return gemm_cfg<T, false, 2, 8, 2>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
+    return gemm_cfg<T, false, 2, 4, 2>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
+  }
 }
 
 hipError_t launch_gemm(bool bf16_io, bool a_trans, const void* A, int lda, size_t sA, const void* Bm, int ldb,
@@ -346,6 +503,43 @@ hipError_t launch_expand(bool bf16_io, const void* At, int ldA, const void* Bz, 
                          void* out, hipStream_t st) {
   return bf16_io ? expand_t<bf16>(At, ldA, Bz, B, R, L, C, out, st)
                  : expand_t<float>(At, ldA, Bz, B, R, L, C, out, st);
+}
+
+template <class T, int MTA, int KS>
+static hipError_t gx_fused_cfg(const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L, int Cy,
+                               int Cx, void* out, hipStream_t st) {
+  constexpr int NW = 4;
+  dim3 grid((Cx + 127) / 128, B);
+  hipLaunchKernelGGL((gx_fused_kernel<T, MTA, KS, NW>), grid, dim3(NW * WAVE), 0, st, (const T*)Qgy, (const T*)w,
+                     (const T*)At, ldA, R, L, Cy, Cx, (T*)out);
+  return hipGetLastError();
+}
+
+template <class T>
+static hipError_t gx_fused_t(const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L, int Cy,
+                             int Cx, void* out, hipStream_t st) {
+  const int mta = (R + 15) / 16;
+  const int ks = (R + MM<T>::KSTEP - 1) / MM<T>::KSTEP;
+#define GXF(MA, K)                                                                        \
+  if (mta == MA && ks == K) return gx_fused_cfg<T, MA, K>(Qgy, w, At, ldA, B, R, L, Cy, Cx, out, st);
+  if constexpr (MM<T>::KSTEP == 32) {
+    GXF(1, 1) GXF(2, 1) GXF(3, 2) GXF(4, 2)
+  } else {
+    GXF(1, 1) GXF(2, 2) GXF(3, 3) GXF(4, 4)
+  }
+#undef GXF
+  return hipErrorInvalidValue;
+}
+
+bool gx_fused_applies(bool bf16_io, int B, int Cx, int Cy) {
+  const double wbytes = (double)Cx * Cy * (bf16_io ? 2 : 4);
+  return wbytes <= 2.0 * (1 << 20) && B * wbytes <= 64.0 * (1 << 20);
+}
+
+hipError_t launch_gx_fused(bool bf16_io, const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L,
+                           int Cy, int Cx, void* out, hipStream_t st) {
+  return bf16_io ? gx_fused_t<bf16>(Qgy, w, At, ldA, B, R, L, Cy, Cx, out, st)
+                 : gx_fused_t<float>(Qgy, w, At, ldA, B, R, L, Cy, Cx, out, st);
 }
 
 }  // namespace instant

@@ -23,6 +23,12 @@ hipError_t launch_gemm(bool bf16_io, bool a_trans, const void* A, int lda, size_
 hipError_t launch_expand(bool bf16_io, const void* At, int ldA, const void* Bz, int B, int R, int L, int C,
                          void* out, hipStream_t st);
 
+// gx[b][l][c] = sum_r At[l][r] (sum_k Qgy[b][r][k] w[k][c]) in one kernel, g_hat_x kept in
+// LDS (rounded to the I/O dtype). Applies when w is small enough to stay in L2.
+bool gx_fused_applies(bool bf16_io, int B, int Cx, int Cy);
+hipError_t launch_gx_fused(bool bf16_io, const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L,
+                           int Cy, int Cx, void* out, hipStream_t st);
+
 // ---- calibration ([KD1], [KD2])
 
 // Upper-triangle tile partial sums of sum_b X_b X_b^T over `nsplit` slices of the

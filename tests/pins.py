@@ -298,9 +298,25 @@ def check_autocorrelation(O, seed=11):
     assert np.allclose(acc.mean(), acc.mean().T, rtol=0, atol=0)
 
 
+def check_autocorr_entries(O, seed=12):
+    """Sampled entries equal the full statistic's entries (and its symmetry)."""
+    rng = np.random.default_rng(seed)
+    t1 = rng.standard_normal((3, 7, 4))
+    t2 = rng.standard_normal((2, 7, 4))
+    acc = O.Accumulator(7)
+    acc.add(t1)
+    acc.add(t2)
+    rows = rng.integers(0, 7, 20)
+    cols = rng.integers(0, 7, 20)
+    got = O.autocorr_entries([t1, t2], rows, cols)
+    assert np.abs(got - acc.mean()[rows, cols]).max() < 1e-13
+    assert np.abs(got - O.autocorr_entries([t1, t2], cols, rows)).max() == 0.0
+
+
 ALL_CHECKS = [
     check_full_rank_identity, check_reordering, check_truncation_golden,
     check_truncation_bruteforce, check_truncation_through_matrix, check_error_semantics,
     check_flop_formula, check_eigen_invariants, check_exact_lowrank_recovery,
     check_compensation_algebra, check_monotone_in_p, check_memory_count, check_autocorrelation,
+    check_autocorr_entries,
 ]
