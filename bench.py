@@ -28,6 +28,26 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "proj_bert_attn_traffic.json")
+
+
+def measured_traffic():
+    """HBM bytes per forward-compression launch from the recorded rocprofv3 counters
+    (FETCH_SIZE and WRITE_SIZE scaled by a copy kernel of known size), or None when the
+    kernel sources changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["sources_sha256"]:
+            return None
+        return rec["traffic_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -40,6 +60,9 @@ def parse():
                     help="distinct resident batches cycled through (more than N_cal, so consecutive "
                          "calibration windows see different statistics)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before the timed region, copy a buffer of this many MiB three times (a plain "
+                         "copy kernel of known size that scales the profiler's byte counters)")
     ap.add_argument("--cpu-sample", type=int, default=8, help="samples of a batch the oracle times")
     return ap.parse_args()
 
@@ -85,6 +108,15 @@ def main():
     xhat = torch.empty((B, R_max, Cx), dtype=tdt, device=dev)
     gw = torch.empty((Cy, Cx), dtype=tdt, device=dev)
     gx = torch.empty((B, L, Cx), dtype=tdt, device=dev)
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # initial calibration (set-up, untimed)
     for t in range(wl.n_cal):
@@ -178,7 +210,7 @@ def main():
         },
         "roofline": {"kernel": "proj (forward compression x_hat = P x)", "bound": "hbm",
                      "achieved": gbs_fwd, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs_fwd / HBM_PEAK_GBS, "traffic": None,
+                     "frac": gbs_fwd / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "algorithmic_bytes_per_launch": bytes_fwd},
     }
 

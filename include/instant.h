@@ -24,12 +24,11 @@
  * Conventions
  *   - Every pointer named as "device" is owned by the caller. The library never
  *     allocates device memory: all device state lives in the caller's workspace
- *     (instant_workspace_bytes). The host handle and one small pinned host block
- *     are the library's own.
- *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*; NULL is
- *     the default stream) except instant_query, which waits for the last
- *     calibration result, and the first compress/backward call after a finalize,
- *     which waits once for the new ranks (Rx, Ry size the launches).
+ *     (instant_workspace_bytes). The host handle is the library's own.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL is the
+ *     default stream), except a finalizing instant_calibrate, which returns only when
+ *     the new projections (or the failure) are known: the ranks Rx, Ry it decides size
+ *     every later launch. A finalize happens once per N_t steps ([Framework]).
  *   - Host-detectable errors return at once with no side effect.
  *     Device-detected calibration failures are latched; the previous projections
  *     stay active and instant_query reports the failure.
@@ -112,7 +111,9 @@ instant_status instant_destroy(instant_layer* h);
  * finalize != 0 then turns both sums into means over the samples seen, takes the
  * eigen-decomposition of each, truncates at the energy threshold with p extra
  * bases, applies the compensation ([KD2]), publishes the new P and Q and clears
- * the sums. A finalize needs samples on both sides. */
+ * the sums. A finalize needs samples on both sides (else E_STATE). It returns the
+ * finalize's status: E_ENERGY, E_NONFINITE, E_NOCONV or E_RANK leave the previous
+ * projections active. B may be 0 when x and gy are both NULL. */
 instant_status instant_calibrate(instant_layer* h, const void* x, const void* gy, int32_t B,
                                  int32_t finalize, void* stream);
 
@@ -128,8 +129,8 @@ instant_status instant_compress_fwd(instant_layer* h, const void* x, int32_t B, 
 instant_status instant_backward(instant_layer* h, const void* xhat, const void* gy, const void* w,
                                 int32_t B, void* gw, void* gx, void* stream);
 
-/* Wait for the last finalize (if any is pending) and report its result. Returns
- * the latched device status of that finalize (INSTANT_OK if none failed). */
+/* Report the result of the last finalize (ranks, compensation, sweeps, status).
+ * Returns that finalize's status (INSTANT_OK if none has failed). Host only. */
 instant_status instant_query(instant_layer* h, instant_info* out);
 
 /* Install projections directly (float32 device arrays P [Rx, L], Q [Ry, L]) with

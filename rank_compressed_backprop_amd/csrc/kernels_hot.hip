@@ -398,7 +398,8 @@ __global__ __launch_bounds__(NW * WAVE) void gx_fused_kernel(const T* __restrict
 template <class T, int MT, int NW, int SW>
 static hipError_t proj_cfg(const void* A, int ldA, int M, int M0, const void* X, int B, int L, int C, void* out0,
                            void* out1, hipStream_t st) {
-  constexpr int U = MT <= 2 ? 4 : (MT <= 5 ? 2 : 1);  // loads in flight vs registers
+  // loads in flight vs registers; with eight waves a strip is already split finely
+  constexpr int U = NW >= 8 ? (MT <= 2 ? 2 : 1) : (MT <= 2 ? 4 : (MT <= 5 ? 2 : 1));
   dim3 grid((C + 16 * SW - 1) / (16 * SW), B);
   hipLaunchKernelGGL((proj_kernel<T, MT, NW, U, SW>), grid, dim3(NW * WAVE), 0, st, (const T*)A, ldA, M, M0,
                      (const T*)X, L, C, (T*)out0, (T*)out1);
@@ -409,8 +410,14 @@ template <class T, int MT>
 static hipError_t proj_mt(const void* A, int ldA, int M, int M0, const void* X, int B, int L, int C, void* out0,
                           void* out1, hipStream_t st) {
   const int nsteps = (L + MM<T>::KSTEP - 1) / MM<T>::KSTEP;
-  // narrower strips when 128-column strips would leave compute units idle
-  const bool narrow = (long)((C + 127) / 128) * B < 256 && C > 64;
+  // eight waves per strip keep the most loads in flight per compute unit (measured on
+  // gfx950 at B=32, L=512, C=768); narrower strips when 128-column strips would leave
+  // compute units idle and the token axis is short
+  const bool narrow = (long)((C + 127) / 128) * B < 256 && C > 64 && nsteps < 8;
+  // (512-thread blocks leave 256 registers per lane: only the narrow stacks fit)
+  if constexpr (MT <= 2) {
+    if (nsteps >= 8) return proj_cfg<T, MT, 8, 8>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
+  }
   if (nsteps >= 4)
     return narrow ? proj_cfg<T, MT, 4, 4>(A, ldA, M, M0, X, B, L, C, out0, out1, st)
                   : proj_cfg<T, MT, 4, 8>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
@@ -508,7 +515,7 @@ hipError_t launch_expand(bool bf16_io, const void* At, int ldA, const void* Bz, 
 template <class T, int MTA, int KS>
 static hipError_t gx_fused_cfg(const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L, int Cy,
                                int Cx, void* out, hipStream_t st) {
-  constexpr int NW = 4;
+  constexpr int NW = MTA == 1 ? 8 : 4;  // 512-thread blocks only where the registers fit
   dim3 grid((Cx + 127) / 128, B);
   hipLaunchKernelGGL((gx_fused_kernel<T, MTA, KS, NW>), grid, dim3(NW * WAVE), 0, st, (const T*)Qgy, (const T*)w,
                      (const T*)At, ldA, R, L, Cy, Cx, (T*)out);
