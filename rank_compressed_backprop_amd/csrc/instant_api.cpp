@@ -23,8 +23,9 @@ using namespace instant;
 constexpr int MAX_L = 2048;  // a Jacobi pair stages 16 columns of L floats in LDS
 constexpr int MAX_R = 64;
 constexpr int LD_QT = 64;
-constexpr int SYRK_TARGET_BLOCKS = 1024;
+constexpr int SYRK_TARGET_BLOCKS = 256;  // one 128x128 tile-slice per compute unit
 constexpr int SYRK_MAX_SPLIT = 64;
+constexpr int SYRK_TILE = 128;
 
 inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
@@ -48,7 +49,7 @@ bool config_ok(const instant_config* c) {
 }
 
 struct Layout {
-  size_t SX, SG, part, eig, sig_x, sig_g, info, rank, P32[2], Q32[2], PQ[2], Qt[2], Pgy, Qgy, gxh, total;
+  size_t SX, SG, zpad, part, eig, sig_x, sig_g, info, rank, P32[2], Q32[2], PQ[2], Qt[2], Pgy, Qgy, gxh, total;
   int ldL;
 };
 
@@ -65,7 +66,8 @@ Layout layout_of(const instant_config* c) {
   };
   l.SX = take(L * L * sizeof(double));
   l.SG = take(L * L * sizeof(double));
-  l.part = take((size_t)syrk_split_cap(c->L) * syrk_tiles(c->L) * 64 * 64 * sizeof(float));
+  l.zpad = take(256);
+  l.part = take((size_t)syrk_split_cap(c->L) * syrk_tiles(c->L) * SYRK_TILE * SYRK_TILE * sizeof(float));
   l.eig = take(eig_workspace_bytes(c->L));
   l.sig_x = take(L * sizeof(float));
   l.sig_g = take(L * sizeof(float));
@@ -115,13 +117,14 @@ inline hipStream_t S(void* stream) { return (hipStream_t)stream; }
 inline instant_status hip_ok(hipError_t e) { return e == hipSuccess ? INSTANT_OK : INSTANT_E_HIP; }
 
 instant_status accumulate(instant_layer* h, const void* t, int B, int C, double* Sacc, hipStream_t st) {
-  const int steps = (C + (h->bf16 ? 32 : 16) - 1) / (h->bf16 ? 32 : 16);
+  const int kstep = h->bf16 ? 32 : 16;
+  const int steps = (C + kstep - 1) / kstep;
   const long total = (long)B * steps;
-  // every wave of a slice gets at least U = 4 steps; a multiple of 8 slices when there
-  // are that many (one XCD per slice)
-  int nsplit = (int)std::min<long>(syrk_split_cap(h->cfg.L), std::max<long>(1, total / 16));
+  // slices of at least 32 k-steps (the LDS pipeline's fill is then small), enough of them
+  // to give every compute unit a tile-slice, a multiple of 8 when there are 16 or more
+  int nsplit = (int)std::min<long>(syrk_split_cap(h->cfg.L), std::max<long>(1, total / 32));
   if (nsplit >= 16) nsplit -= nsplit % 8;
-  hipError_t e = launch_syrk(h->bf16, t, B, h->cfg.L, C, nsplit, h->part(), st);
+  hipError_t e = launch_syrk(h->bf16, t, B, h->cfg.L, C, nsplit, h->ws + h->lay.zpad, h->part(), st);
   if (e != hipSuccess) return INSTANT_E_HIP;
   return hip_ok(launch_syrk_reduce(h->part(), nsplit, h->cfg.L, Sacc, st));
 }
@@ -151,6 +154,7 @@ INSTANT_API instant_status instant_create(instant_layer** h, const instant_confi
   L->last = INSTANT_OK;
   // statistics start at zero; the rest of the workspace is written before it is read
   hipError_t e = launch_zero(L->SX(), (size_t)cfg->L * cfg->L * sizeof(double), S(stream));
+  if (e == hipSuccess) e = launch_zero(L->ws + L->lay.zpad, 256, S(stream));
   if (e == hipSuccess) e = launch_zero(L->SG(), (size_t)cfg->L * cfg->L * sizeof(double), S(stream));
   if (e != hipSuccess) {
     delete L;
@@ -275,12 +279,13 @@ INSTANT_API instant_status instant_backward(instant_layer* h, const void* xhat, 
   void* gxh = h->ws + h->lay.gxh;
   // [P; Q] gy_b from one pass over gy
   hipError_t e = launch_proj(h->bf16, h->PQ(a), h->lay.ldL, Rx + Ry, Rx, gy, B, L, Cy, Pgy, Qgy, st);
-  // g_w = sum_b (P gy_b)^T x_hat_b: M = Cy, N = Cx, K = B * Rx
-  if (e == hipSuccess) e = launch_gemm(h->bf16, true, Pgy, Cy, 0, xhat, Cx, 0, gw, Cx, 0, 1, Cy, Cx, B * Rx, st);
   if (gx_fused_applies(h->bf16, B, Cx, Cy)) {
-    // g_x_b = Q^T ((Q gy_b) w) in one kernel, w resident in L2
-    if (e == hipSuccess) e = launch_gx_fused(h->bf16, Qgy, w, h->Qt(a), LD_QT, B, Ry, L, Cy, Cx, gx, st);
+    // g_x_b = Q^T ((Q gy_b) w) with w resident in L2, and g_w, in one launch
+    if (e == hipSuccess)
+      e = launch_bwd_tail(h->bf16, Qgy, w, h->Qt(a), LD_QT, B, Ry, L, Cy, Cx, gx, Pgy, xhat, gw, B * Rx, st);
   } else {
+    // g_w = sum_b (P gy_b)^T x_hat_b: M = Cy, N = Cx, K = B * Rx
+    if (e == hipSuccess) e = launch_gemm(h->bf16, true, Pgy, Cy, 0, xhat, Cx, 0, gw, Cx, 0, 1, Cy, Cx, B * Rx, st);
     // g_hat_x = (Q gy) w: M = B * Ry, N = Cx, K = Cy
     if (e == hipSuccess) e = launch_gemm(h->bf16, false, Qgy, Cy, 0, w, Cx, 0, gxh, Cx, 0, 1, B * Ry, Cx, Cy, st);
     // g_x_b = Q^T g_hat_x_b

@@ -11,7 +11,19 @@
 namespace instant {
 
 // ============================================================================ SYRK
-constexpr int ST = 64;  // statistics tile edge
+// Running sums S += sum_b X_b X_b^T over upper-triangle 128x128 tiles. A block of four
+// waves owns one tile and one slice of the (sample, channel) reduction; each wave owns a
+// 64x64 quarter. A k-step covers 64 bytes of every row (32 bf16 / 16 fp32 values); the
+// two row panels of a step (128 rows x 64 bytes each; one panel for diagonal tiles) go
+// straight from memory to LDS (global_load_lds, 16 bytes per lane) through an
+// SYRK_STAGES-deep ring, so several steps' loads are in flight while the matrix cores
+// consume the oldest. Within a panel, 16-byte chunk c of row r sits in slot
+// c ^ ((r >> 2) & 3), which makes the fragment reads bank-conflict-free. Lanes whose
+// row or channel is out of range read a zeroed pad instead. Slices write float32
+// partial tiles; a second kernel adds them to the float64 sums in slice order.
+constexpr int ST = 128;           // statistics tile edge
+constexpr int SYRK_STAGES = 4;    // LDS ring depth
+constexpr int PANEL = ST * 64;    // bytes per panel
 
 int syrk_tiles(int L) {
   const int T = (L + ST - 1) / ST;
@@ -27,97 +39,137 @@ __device__ inline void upper_tile(int idx, int T, int& ti, int& tj) {
   tj = ti + idx;
 }
 
-// part[s][tile][64*64] = sum over the s-th slice of the (sample, channel-step) range of
-// X_b[rows of ti] . X_b[rows of tj]^T. Four waves split the slice; LDS sums them in order.
+// 16 bytes per lane from src straight into LDS at lds_wave + 16 * lane (lds_wave uniform
+// across the wave). Kept out of the kernel body: target builtins there would keep the host
+// pass from emitting the kernel's launch stub.
+__device__ inline void lds_dma16(const void* src, void* lds_wave) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave, 16, 0, 0);
+}
+
+// Workgroup barrier without a memory fence (waits are explicit around it).
+__device__ inline void bare_barrier() {
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding, and for all of its
+// LDS reads: the next barrier may hand their buffer to a refill.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+}
+
 template <class T>
 __global__ __launch_bounds__(256) void syrk_kernel(const T* __restrict__ X, int B, int L, int C, int nsplit,
-                                                   float* __restrict__ part) {
+                                                   const T* __restrict__ zpad, float* __restrict__ part) {
   typedef MM<T> mm;
   typedef typename mm::frag frag;
-  constexpr int NW = 4;
-  const int lane = threadIdx.x & (WAVE - 1);
-  const int wave = threadIdx.x / WAVE;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[SYRK_STAGES][2][PANEL];
+  const int tid = threadIdx.x;
+  const int lane = tid & (WAVE - 1);
+  const int wave = tid / WAVE;
   const int Tn = (L + ST - 1) / ST;
   const int ntiles = Tn * (Tn + 1) / 2;
-  // Workgroups are dealt to the 8 XCDs round-robin by linear id. When there are at least
-  // 8 slices, give all tiles of a slice to one XCD so each sample is fetched into one L2.
+  // Workgroups are dealt to the 8 XCDs round-robin by linear id. With a multiple of 8
+  // slices, all tiles of a slice run on one XCD, so each sample is fetched into one L2.
   int tile, s;
   const int lin = blockIdx.x;
   if (nsplit % 8 == 0) {
-    const int xcd = lin % 8, k = lin / 8;
-    s = xcd + 8 * (k / ntiles);
-    tile = k % ntiles;
+    const int xcd = lin % 8, kq = lin / 8;
+    s = xcd + 8 * (kq / ntiles);
+    tile = kq % ntiles;
   } else {
     s = lin / ntiles;
     tile = lin % ntiles;
   }
   int ti, tj;
   upper_tile(tile, Tn, ti, tj);
+  const bool diag = ti == tj;
   const int steps_c = (C + mm::KSTEP - 1) / mm::KSTEP;
-  const long total = (long)B * steps_c;
-  const long beg = total * s / nsplit;
-  const long end = total * (s + 1) / nsplit;
-  const int kl = mm::G * (lane >> 4);
+  const int total = B * steps_c;
+  const int beg = (int)((long)total * s / nsplit);
+  const int end = (int)((long)total * (s + 1) / nsplit);
+  const int nq = end - beg;
 
+  // Each wave moves 1 KB of a panel per instruction: rows 16*j + lane/4 of wave-load j.
+  // Wave w issues wave-loads j = 2w, 2w+1 of each panel.
+  constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  auto issue = [&](int q, int stage) {
+    const int b = q / steps_c;
+    const int k0 = (q - b * steps_c) * mm::KSTEP;
+    const T* __restrict__ Xb = X + (size_t)b * L * C;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if (p == 1 && diag) break;
+      const int tb = p == 0 ? ti : tj;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = 2 * wave + h;
+        const int rloc = 16 * j + (lane >> 2);
+        const int chunk = (lane & 3) ^ ((rloc >> 2) & 3);
+        const int row = tb * ST + rloc;
+        const int kk = k0 + chunk * EPC;
+        const T* src = (row < L && kk < C) ? Xb + (size_t)row * C + kk : zpad;
+        lds_dma16(src, &lds[stage][p][1024 * j]);
+      }
+    }
+  };
+
+  const int wr = wave >> 1, wc = wave & 1;  // this wave's 64x64 quarter
   f32x4 acc[4][4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc[t][u] = zero4();
 
-  constexpr int U = 4;  // k-steps whose loads are in flight together
-  for (long q0 = beg + wave; q0 < end; q0 += NW * U) {
-    frag a[U][4], bb[U][4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const long q = q0 + u * NW;
-      const bool qok = q < end;
-      const int b = qok ? (int)(q / steps_c) : 0;
-      const int kk = (int)(q % steps_c) * mm::KSTEP + kl;
-      const T* __restrict__ Xb = X + (size_t)b * L * C;
-      const bool kok = qok && kk < C;
+  for (int st = 0; st < SYRK_STAGES - 1; ++st)
+    if (st < nq) issue(beg + st, st);
+  const int g = lane >> 4;  // this lane's k-group
+  for (int i = 0; i < nq; ++i) {
+    // stage i has landed once at most the loads of the younger stages are outstanding
+    const int younger = (nq - 1 - i) < (SYRK_STAGES - 2) ? (nq - 1 - i) : (SYRK_STAGES - 2);
+    if (diag) {
+      if (younger >= 2) wait_vmcnt<4>();
+      else if (younger == 1) wait_vmcnt<2>();
+      else wait_vmcnt<0>();
+    } else {
+      if (younger >= 2) wait_vmcnt<8>();
+      else if (younger == 1) wait_vmcnt<4>();
+      else wait_vmcnt<0>();
+    }
+    // Bare s_barrier: every wave has waited for its own loads of stage i above, and a
+    // __syncthreads fence would also drain the younger stages still in flight.
+    bare_barrier();
+    // the stage read last iteration is free again: refill it
+    if (i + SYRK_STAGES - 1 < nq) issue(beg + i + SYRK_STAGES - 1, (i + SYRK_STAGES - 1) % SYRK_STAGES);
+    const unsigned char* pa = lds[i % SYRK_STAGES][0];
+    const unsigned char* pb = diag ? pa : lds[i % SYRK_STAGES][1];
+    frag af[4], bf[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r = ti * ST + 16 * t + (lane & 15);
-        a[u][t] = load_frag<T>(Xb + (size_t)r * C + kk, kok && r < L);
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r = tj * ST + 16 * t + (lane & 15);
-        bb[u][t] = load_frag<T>(Xb + (size_t)r * C + kk, kok && r < L);
-      }
+    for (int t = 0; t < 4; ++t) {
+      const int ra = 64 * wr + 16 * t + (lane & 15);
+      const int rb = 64 * wc + 16 * t + (lane & 15);
+      af[t] = *reinterpret_cast<const frag*>(pa + ra * 64 + 16 * (g ^ ((ra >> 2) & 3)));
+      bf[t] = *reinterpret_cast<const frag*>(pb + rb * 64 + 16 * (g ^ ((rb >> 2) & 3)));
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[t][v] = mm::mma(a[u][t], bb[u][v], acc[t][v]);
+      for (int u = 0; u < 4; ++u) acc[t][u] = mm::mma(af[t], bf[u], acc[t][u]);
   }
 
-  __shared__ float red[NW][4][4][WAVE];
   float* __restrict__ out = part + ((size_t)s * ntiles + tile) * (ST * ST);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[wave][u][v][lane] = acc[t][u][v];
-    __syncthreads();
-    {
-      const int v = wave;  // each wave finishes one of the four rows a lane holds
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float sum = red[0][u][v][lane];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) sum += red[w][u][v][lane];
-        const int row = 16 * t + 4 * (lane >> 4) + v;
-        const int col = 16 * u + (lane & 15);
-        out[row * ST + col] = sum;
+      for (int v = 0; v < 4; ++v) {
+        const int row = 64 * wr + 16 * t + 4 * (lane >> 4) + v;
+        const int col = 64 * wc + 16 * u + (lane & 15);
+        out[row * ST + col] = acc[t][u][v];
       }
-    }
-    __syncthreads();
-  }
 }
 
 // S[i][j] += sum_s part[s][tile] in split order, float64, for the upper-triangle tiles.
@@ -149,18 +201,21 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
 }
 
 template <class T>
-static hipError_t syrk_t(const void* X, int B, int L, int C, int nsplit, float* part, hipStream_t st) {
+static hipError_t syrk_t(const void* X, int B, int L, int C, int nsplit, const void* zpad, float* part,
+                         hipStream_t st) {
   dim3 grid(syrk_tiles(L) * nsplit);
-  hipLaunchKernelGGL(syrk_kernel<T>, grid, dim3(256), 0, st, (const T*)X, B, L, C, nsplit, part);
+  hipLaunchKernelGGL(syrk_kernel<T>, grid, dim3(256), 0, st, (const T*)X, B, L, C, nsplit, (const T*)zpad, part);
   return hipGetLastError();
 }
 
-hipError_t launch_syrk(bool bf16_io, const void* X, int B, int L, int C, int nsplit, float* part, hipStream_t st) {
-  return bf16_io ? syrk_t<bf16>(X, B, L, C, nsplit, part, st) : syrk_t<float>(X, B, L, C, nsplit, part, st);
+hipError_t launch_syrk(bool bf16_io, const void* X, int B, int L, int C, int nsplit, const void* zpad, float* part,
+                       hipStream_t st) {
+  return bf16_io ? syrk_t<bf16>(X, B, L, C, nsplit, zpad, part, st)
+                 : syrk_t<float>(X, B, L, C, nsplit, zpad, part, st);
 }
 
 hipError_t launch_syrk_reduce(const float* part, int nsplit, int L, double* S, hipStream_t st) {
-  dim3 grid(syrk_tiles(L), ST * ST / 256);
+  dim3 grid(syrk_tiles(L), ST * ST / 256);  // 64 blocks of 256 elements per tile
   hipLaunchKernelGGL(syrk_reduce_kernel, grid, dim3(256), 0, st, part, nsplit, syrk_tiles(L), L, S);
   return hipGetLastError();
 }

@@ -20,6 +20,8 @@
 // always drains.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -69,6 +71,7 @@ constexpr size_t EIG_FLAGS_BYTES = 256;
 struct EigBufs {
   float* W[2];
   float* Wtmp;      // statistic in float32 before the warm start product
+  float* V32;       // the accumulated rotation in float32, for that product
   double* V[2];
   float* nrm[2];
   int* flags;
@@ -84,6 +87,8 @@ static EigBufs eig_bufs(void* work, const EigLayout& e) {
   b.W[1] = (float*)p;
   p += e.wbytes;
   b.Wtmp = (float*)p;
+  p += e.wbytes;
+  b.V32 = (float*)p;
   p += e.wbytes;
   b.V[0] = (double*)p;
   p += e.vbytes;
@@ -105,7 +110,7 @@ static EigBufs eig_bufs(void* work, const EigLayout& e) {
 
 size_t eig_workspace_bytes(int L) {
   const EigLayout e = eig_layout(L);
-  return 3 * e.wbytes + 2 * e.vbytes + 2 * e.nrmbytes + EIG_FLAGS_BYTES + e.verbytes + 2 * e.colbytes;
+  return 4 * e.wbytes + 2 * e.vbytes + 2 * e.nrmbytes + EIG_FLAGS_BYTES + e.verbytes + 2 * e.colbytes;
 }
 
 // ---------------------------------------------------------------------------- set-up kernels
@@ -133,53 +138,11 @@ __global__ __launch_bounds__(256) void identity_kernel(double* __restrict__ V, i
   for (int r = threadIdx.x; r < ldw; r += 256) V[(size_t)c * ldw + r] = (r == c) ? 1.0 : 0.0;
 }
 
-// Warm start: W = C V on the float32 matrix cores, C symmetric (float32, column-major in
-// Ct), V read from its float64 master (column-major). Output tile: 16*4 columns of W x 128
-// rows; D[c][r] = sum_k V[k][c] C[r][k], A = V^T (k contiguous), B = C (r contiguous).
-// Rounding V to float32 here only perturbs W at float32 resolution; the accumulated
-// rotation itself stays float64.
-__global__ __launch_bounds__(64) void warm_gemm_kernel(const float* __restrict__ Ct, const double* __restrict__ V,
-                                                       int L, int ldw, int ncols, float* __restrict__ W) {
-  typedef MM<float> mm;
-  const int lane = threadIdx.x;
-  const int rcol = blockIdx.x * 128 + 8 * (lane & 15);  // W row (B operand column)
-  const int c0 = blockIdx.y * 64;                       // W column block
-  const bool r_ok = rcol < ldw;
-  const int kl = mm::G * (lane >> 4);
-  f32x4 acc[4][8];
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[t][j] = zero4();
-  for (int k0 = 0; k0 < L; k0 += mm::KSTEP) {
-    mm::frag bf[8];
-    load_strip_T<float, 8>(Ct, ldw, k0 + kl, L, rcol, r_ok, bf);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int c = c0 + 16 * t + (lane & 15);
-      mm::frag af;
-#pragma unroll
-      for (int g = 0; g < mm::G; ++g) {
-        const int k = k0 + kl + g;
-        af[g] = (c < ncols && k < L) ? (float)V[(size_t)c * ldw + k] : 0.0f;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[t][j] = mm::mma(af, bf[j], acc[t][j]);
-    }
-  }
-  if (!r_ok) return;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int c = c0 + 16 * t + 4 * (lane >> 4) + v;
-      if (c < ncols) {
-        float o[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = acc[t][j][v];
-        store_row<float, 8>(W + (size_t)c * ldw + rcol, o);
-      }
-    }
+// Warm start, step 1: the accumulated rotation rounded to float32 (column-major, as stored).
+// Rounding V here only perturbs W = C V at float32 resolution; the rotation itself stays
+// float64.
+__global__ __launch_bounds__(256) void v_to_f32_kernel(const double* __restrict__ V, size_t n, float* __restrict__ V32) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) V32[i] = (float)V[i];
 }
 
 // Column norms of W: sigma_c = ||W[:, c]||, c < L.
@@ -721,8 +684,14 @@ hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv
     if (warm) {
       hipLaunchKernelGGL(jacobi_prep_kernel, dim3(e.ncols), dim3(256), 0, st, S[s], inv[s], L, e.ldw, b.Wtmp,
                          flags + F_BAD + s);
-      hipLaunchKernelGGL(warm_gemm_kernel, dim3((e.ldw + 127) / 128, (e.ncols + 63) / 64), dim3(64), 0, st, b.Wtmp,
-                         b.V[s], L, e.ldw, e.ncols, b.W[s]);
+      // W[c][r] = sum_k V[k][c] C[k][r]: A = V^T stored [ncols][ldw] (k contiguous), B = C
+      // stored [k][r] (r contiguous), both float32, on the matrix cores
+      const size_t nv = (size_t)e.ncols * e.ldw;
+      hipLaunchKernelGGL(v_to_f32_kernel, dim3((unsigned)std::min<size_t>((nv + 255) / 256, 2048)), dim3(256), 0, st,
+                         b.V[s], nv, b.V32);
+      if ((err = launch_gemm(false, false, b.V32, e.ldw, 0, b.Wtmp, e.ldw, 0, b.W[s], e.ldw, 0, 1, e.ncols, e.ldw, L,
+                             st)) != hipSuccess)
+        return err;
     } else {
       hipLaunchKernelGGL(jacobi_prep_kernel, dim3(e.ncols), dim3(256), 0, st, S[s], inv[s], L, e.ldw, b.W[s],
                          flags + F_BAD + s);

@@ -113,23 +113,24 @@ __global__ __launch_bounds__(NW * WAVE) void proj_kernel(const T* __restrict__ A
 // B is [K][ldb] (n contiguous); the wave covers 128 columns.
 // Grid: (ceil(N / 128), ceil(M / rows per wave), batch); the NW waves of a block split K,
 // each issuing the loads of U steps before any product.
+// Block (bx, by, bz) of the grid described above; `red` is NW * 8 KB of LDS.
 template <class T, bool A_TRANS, int MT, int NW, int U>
-__global__ __launch_bounds__(NW * WAVE) void gemm_kernel(const T* __restrict__ A, int lda, size_t strideA,
-                                                         const T* __restrict__ Bm, int ldb, size_t strideB,
-                                                         T* __restrict__ Cm, int ldc, size_t strideC,
-                                                         int M, int N, int K) {
+__device__ __forceinline__ void gemm_block(const T* __restrict__ A, int lda, size_t strideA,
+                                           const T* __restrict__ Bm, int ldb, size_t strideB, T* __restrict__ Cm,
+                                           int ldc, size_t strideC, int M, int N, int K, int bx, int by, int bz,
+                                           float (*red)[8][4][WAVE]) {
   typedef MM<T> mm;
   typedef typename mm::frag frag;
   const int lane = threadIdx.x & (WAVE - 1);
   const int wave = threadIdx.x / WAVE;
-  const int z = blockIdx.z;
+  const int z = bz;
   A += z * strideA;
   Bm += z * strideB;
   Cm += z * strideC;
-  const int col = blockIdx.x * 128 + 8 * (lane & 15);
+  const int col = bx * 128 + 8 * (lane & 15);
   const bool col_ok = col < N;
   constexpr int ROWS = A_TRANS ? 64 : 16 * MT;
-  const int m0 = blockIdx.y * ROWS;
+  const int m0 = by * ROWS;
   const int kl = mm::G * (lane >> 4);
 
   f32x4 acc[MT][8];
@@ -194,7 +195,6 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_kernel(const T* __restrict__ A
         store(row_of(t, v), o);
       }
   } else {
-    __shared__ float red[NW][8][4][WAVE];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
 #pragma unroll
@@ -216,6 +216,16 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_kernel(const T* __restrict__ A
       __syncthreads();
     }
   }
+}
+
+template <class T, bool A_TRANS, int MT, int NW, int U>
+__global__ __launch_bounds__(NW * WAVE) void gemm_kernel(const T* __restrict__ A, int lda, size_t strideA,
+                                                         const T* __restrict__ Bm, int ldb, size_t strideB,
+                                                         T* __restrict__ Cm, int ldc, size_t strideC,
+                                                         int M, int N, int K) {
+  __shared__ float red[NW][8][4][WAVE];
+  gemm_block<T, A_TRANS, MT, NW, U>(A, lda, strideA, Bm, ldb, strideB, Cm, ldc, strideC, M, N, K, blockIdx.x,
+                                    blockIdx.y, blockIdx.z, red);
 }
 
 // ----------------------------------------------------------------------------- expand
@@ -281,21 +291,26 @@ __global__ __launch_bounds__(NW * WAVE) void expand_kernel(const T* __restrict__
 // (the NW waves split Cy, LDS sums them), keeps it in LDS in the I/O dtype, and then
 // expands g_x_b[:, strip] = Q^T g_hat_x_b[:, strip] over all L tokens.
 // Grid: (ceil(Cx / 128), B).
+template <class T, int KS>
+struct GxShared {
+  static constexpr int GROWS = KS * MM<T>::KSTEP;  // rows of the LDS operand (zero beyond R)
+  T g[GROWS][128];
+};
+
 template <class T, int MTA, int KS, int NW>
-__global__ __launch_bounds__(NW * WAVE) void gx_fused_kernel(const T* __restrict__ Qgy, const T* __restrict__ w,
-                                                             const T* __restrict__ At, int ldA, int R, int L,
-                                                             int Cy, int Cx, T* __restrict__ out) {
+__device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const T* __restrict__ w,
+                                               const T* __restrict__ At, int ldA, int R, int L, int Cy, int Cx,
+                                               T* __restrict__ out, int strip, int b, float (*red)[8][4][WAVE],
+                                               GxShared<T, KS>& gs) {
   typedef MM<T> mm;
   typedef typename mm::frag frag;
   constexpr int U = 2;
-  constexpr int GROWS = KS * MM<T>::KSTEP;  // rows of the LDS operand (zero beyond R)
-  __shared__ float red[NW][8][4][WAVE];
-  __shared__ __attribute__((aligned(16))) T gsm[GROWS][128];
+  constexpr int GROWS = GxShared<T, KS>::GROWS;
+  auto& gsm = gs.g;
   const int lane = threadIdx.x & (WAVE - 1);
   const int wave = threadIdx.x / WAVE;
-  const int b = blockIdx.y;
   const int lc = 8 * (lane & 15);  // column within the strip
-  const int col = blockIdx.x * 128 + lc;
+  const int col = strip * 128 + lc;
   const bool col_ok = col < Cx;
   const int kl = mm::G * (lane >> 4);
   const T* __restrict__ Ab = Qgy + (size_t)b * R * Cy;
@@ -390,6 +405,38 @@ __global__ __launch_bounds__(NW * WAVE) void gx_fused_kernel(const T* __restrict
         }
       }
     }
+  }
+}
+
+template <class T, int MTA, int KS, int NW>
+__global__ __launch_bounds__(NW * WAVE) void gx_fused_kernel(const T* __restrict__ Qgy, const T* __restrict__ w,
+                                                             const T* __restrict__ At, int ldA, int R, int L,
+                                                             int Cy, int Cx, T* __restrict__ out) {
+  __shared__ float red[NW][8][4][WAVE];
+  __shared__ __attribute__((aligned(16))) GxShared<T, KS> gs;
+  gx_fused_block<T, MTA, KS, NW>(Qgy, w, At, ldA, R, L, Cy, Cx, out, blockIdx.x, blockIdx.y, red, gs);
+}
+
+// The fused g_x blocks and the g_w blocks in one launch: both depend only on the stacked
+// projection, and the g_w tiles fill the compute units the g_x strips leave free.
+// Blocks [0, ngx) are g_x (strip = id % nstrip, sample = id / nstrip); the rest are g_w
+// tiles (64 x 128, K split over the NW waves).
+template <class T, int MTA, int KS, int NW>
+__global__ __launch_bounds__(NW * WAVE) void bwd_tail_kernel(const T* __restrict__ Qgy, const T* __restrict__ w,
+                                                             const T* __restrict__ At, int ldA, int R, int L,
+                                                             int Cy, int Cx, T* __restrict__ gx, int nstrip,
+                                                             int ngx, const T* __restrict__ Pgy,
+                                                             const T* __restrict__ xhat, T* __restrict__ gw,
+                                                             int Kw, int gw_bx) {
+  __shared__ float red[NW][8][4][WAVE];
+  __shared__ __attribute__((aligned(16))) GxShared<T, KS> gs;
+  const int id = blockIdx.x;
+  if (id < ngx) {
+    gx_fused_block<T, MTA, KS, NW>(Qgy, w, At, ldA, R, L, Cy, Cx, gx, id % nstrip, id / nstrip, red, gs);
+  } else {
+    // g_w = sum_b (P gy_b)^T x_hat_b: M = Cy, N = Cx, K = B*Rx (A stored [K][Cy])
+    const int t = id - ngx;
+    gemm_block<T, true, 4, NW, 1>(Pgy, Cy, 0, xhat, Cx, 0, gw, Cx, 0, Cy, Cx, Kw, t % gw_bx, t / gw_bx, 0, red);
   }
 }
 
@@ -536,6 +583,43 @@ static hipError_t gx_fused_t(const void* Qgy, const void* w, const void* At, int
   }
 #undef GXF
   return hipErrorInvalidValue;
+}
+
+template <class T, int MTA, int KS>
+static hipError_t bwd_tail_cfg(const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L, int Cy,
+                               int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw,
+                               hipStream_t st) {
+  constexpr int NW = MTA == 1 ? 8 : 4;
+  const int nstrip = (Cx + 127) / 128;
+  const int ngx = nstrip * B;
+  const int gw_bx = (Cx + 127) / 128, gw_by = (Cy + 63) / 64;
+  hipLaunchKernelGGL((bwd_tail_kernel<T, MTA, KS, NW>), dim3(ngx + gw_bx * gw_by), dim3(NW * WAVE), 0, st,
+                     (const T*)Qgy, (const T*)w, (const T*)At, ldA, R, L, Cy, Cx, (T*)gx, nstrip, ngx, (const T*)Pgy,
+                     (const T*)xhat, (T*)gw, Kw, gw_bx);
+  return hipGetLastError();
+}
+
+template <class T>
+static hipError_t bwd_tail_t(const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L, int Cy,
+                             int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw, hipStream_t st) {
+  const int mta = (R + 15) / 16;
+  const int ks = (R + MM<T>::KSTEP - 1) / MM<T>::KSTEP;
+#define BTC(MA, K) \
+  if (mta == MA && ks == K) return bwd_tail_cfg<T, MA, K>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, st);
+  if constexpr (MM<T>::KSTEP == 32) {
+    BTC(1, 1) BTC(2, 1) BTC(3, 2) BTC(4, 2)
+  } else {
+    BTC(1, 1) BTC(2, 2) BTC(3, 3) BTC(4, 4)
+  }
+#undef BTC
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_tail(bool bf16_io, const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L,
+                           int Cy, int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw,
+                           hipStream_t st) {
+  return bf16_io ? bwd_tail_t<bf16>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, st)
+                 : bwd_tail_t<float>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, st);
 }
 
 bool gx_fused_applies(bool bf16_io, int B, int Cx, int Cy) {

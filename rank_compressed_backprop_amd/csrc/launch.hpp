@@ -29,11 +29,19 @@ bool gx_fused_applies(bool bf16_io, int B, int Cx, int Cy);
 hipError_t launch_gx_fused(bool bf16_io, const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L,
                            int Cy, int Cx, void* out, hipStream_t st);
 
+// The fused g_x of launch_gx_fused and g_w = sum_b Pgy_b^T xhat_b (Pgy [Kw][Cy], xhat
+// [Kw][Cx], Kw = B * Rx) in one launch.
+hipError_t launch_bwd_tail(bool bf16_io, const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L,
+                           int Cy, int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw,
+                           hipStream_t st);
+
 // ---- calibration ([KD1], [KD2])
 
 // Upper-triangle tile partial sums of sum_b X_b X_b^T over `nsplit` slices of the
-// batch*channel reduction, written as float32 to part [nsplit][ntiles][64*64].
-hipError_t launch_syrk(bool bf16_io, const void* X, int B, int L, int C, int nsplit, float* part, hipStream_t st);
+// batch*channel reduction, written as float32 to part [nsplit][ntiles][128*128].
+// zpad: 16 zero bytes in device memory (read in place of out-of-range data).
+hipError_t launch_syrk(bool bf16_io, const void* X, int B, int L, int C, int nsplit, const void* zpad, float* part,
+                       hipStream_t st);
 // S[i][j] += sum_s part[s] (fixed order) for the upper-triangle tiles.
 hipError_t launch_syrk_reduce(const float* part, int nsplit, int L, double* S, hipStream_t st);
 int syrk_tiles(int L);
