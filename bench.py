@@ -162,6 +162,14 @@ def main():
     t_fwd = ev_time(lambda r: lay.compress_fwd(xs[r % nb], B, xhat), reps)
     t_bwd = ev_time(lambda r: lay.backward(xhat, gys[r % nb], w, B, gw, gx), reps)
     t_acc = ev_time(lambda r: lay.calibrate(xs[r % nb], gys[r % nb], B, finalize=False), 50)
+    # host cost of enqueueing one plain step (compress + backward), measured from a drained
+    # queue: when it exceeds the GPU time of a step, the loop above is bound by the host
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    for r in range(50):
+        lay.compress_fwd(xs[r % nb], B, xhat)
+        lay.backward(xhat, gys[r % nb], w, B, gw, gx)
+    t_issue = (time.perf_counter() - h0) / 50
     # one full finalize (eigen-decomposition of both statistics, truncation, publish)
     torch.cuda.synchronize()
     tf0 = time.perf_counter()
@@ -205,7 +213,7 @@ def main():
             "backward_pct_hbm_peak": 100.0 * bytes_bwd / t_bwd / 1e9 / HBM_PEAK_GBS,
             "backward_tokens_per_s": B * L / t_bwd, "backward_TFLOPs": flops_bwd / t_bwd / 1e12,
             "statistics_per_batch_us": t_acc * 1e6,
-            "finalize_ms": t_fin * 1e3, "jacobi_sweeps": [info2.sweeps_x, info2.sweeps_g],
+            "finalize_ms": t_fin * 1e3, "host_enqueue_us_per_plain_step": t_issue * 1e6, "jacobi_sweeps": [info2.sweeps_x, info2.sweeps_g],
             "finalize_status": rcb.instant_status_str(s),
         },
         "roofline": {"kernel": "proj (forward compression x_hat = P x)", "bound": "hbm",

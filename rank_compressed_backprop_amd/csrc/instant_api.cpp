@@ -204,6 +204,26 @@ INSTANT_API instant_status instant_calibrate(instant_layer* h, const void* x, co
   out.sigma_g = (float*)(h->ws + h->lay.sig_g);
   out.info_x = h->info_dev();
   out.info_g = h->info_dev() + INFO_WORDS;
+  // Queued before the host reads the outcome, so the finalize costs one round trip:
+  // the I/O copies of the new projections go to the inactive buffer t (harmless if
+  // the finalize fails: t only becomes active on success), and the statistics window
+  // is consumed whatever the outcome.
+  struct Tail {
+    instant_layer* h;
+    int t;
+  } tail{h, t};
+  out.ctx = &tail;
+  out.before_readback = [](void* ctx, hipStream_t st) -> hipError_t {
+    const Tail& tl = *(const Tail*)ctx;
+    instant_layer* hh = tl.h;
+    hipError_t e = launch_build_io(hh->bf16, hh->P32(tl.t), hh->Q32(tl.t), hh->info_dev() + 2,
+                                   hh->info_dev() + INFO_WORDS + 2, hh->cfg.L, hh->lay.ldL, hh->cfg.R_max,
+                                   hh->PQ(tl.t), hh->Qt(tl.t), LD_QT, st);
+    // SG follows SX in the workspace: one fill clears both (and the padding between)
+    const size_t sbytes = (hh->lay.SG - hh->lay.SX) + (size_t)hh->cfg.L * hh->cfg.L * sizeof(double);
+    if (e == hipSuccess) e = launch_zero(hh->SX(), sbytes, st);
+    return e;
+  };
   int flags[EIG_HOST_FLAGS];
   hipError_t e = run_eig(h->SX(), h->SG(), 1.0 / (double)h->nx, 1.0 / (double)h->ng, h->cfg.L, h->cfg.max_sweeps,
                          h->warm, h->ws + h->lay.eig, out, flags, st);
@@ -211,12 +231,8 @@ INSTANT_API instant_status instant_calibrate(instant_layer* h, const void* x, co
     h->warm = false;
     return INSTANT_E_HIP;
   }
-  int info[2 * INFO_WORDS];
-  e = hipMemcpyAsync(info, h->info_dev(), sizeof(info), hipMemcpyDeviceToHost, st);
-  if (e == hipSuccess) e = hipStreamSynchronize(st);
-  if (e != hipSuccess) return INSTANT_E_HIP;
-  const int* ix = info;
-  const int* ig = info + INFO_WORDS;
+  const int* ix = flags + EIGF_INFO;
+  const int* ig = flags + EIGF_INFO + INFO_WORDS;
   instant_status status = (instant_status)(ix[0] != 0 ? ix[0] : ig[0]);
 
   instant_info& I = h->info;
@@ -235,9 +251,6 @@ INSTANT_API instant_status instant_calibrate(instant_layer* h, const void* x, co
   I.n_samples_x = h->nx;
   I.n_samples_g = h->ng;
   if (status == INSTANT_OK) {
-    e = launch_build_io(h->bf16, h->P32(t), h->Q32(t), h->info_dev() + 2, h->info_dev() + INFO_WORDS + 2, h->cfg.L,
-                        h->lay.ldL, h->cfg.R_max, h->PQ(t), h->Qt(t), LD_QT, st);
-    if (e != hipSuccess) return INSTANT_E_HIP;
     h->active = t;
     h->Rx = ix[2];
     h->Ry = ig[2];
@@ -248,11 +261,7 @@ INSTANT_API instant_status instant_calibrate(instant_layer* h, const void* x, co
   h->last = status;
   // a failed decomposition may leave the accumulated rotation unusable: restart cold
   h->warm = (status == INSTANT_OK || status == INSTANT_E_RANK);
-  // the statistics window is consumed whatever the outcome
   h->nx = h->ng = 0;
-  e = launch_zero(h->SX(), (size_t)h->cfg.L * h->cfg.L * sizeof(double), st);
-  if (e == hipSuccess) e = launch_zero(h->SG(), (size_t)h->cfg.L * h->cfg.L * sizeof(double), st);
-  if (e != hipSuccess) return INSTANT_E_HIP;
   return status;
 }
 

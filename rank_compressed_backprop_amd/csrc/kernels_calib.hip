@@ -22,7 +22,7 @@ namespace instant {
 // row or channel is out of range read a zeroed pad instead. Slices write float32
 // partial tiles; a second kernel adds them to the float64 sums in slice order.
 constexpr int ST = 128;           // statistics tile edge
-constexpr int SYRK_STAGES = 4;    // LDS ring depth
+constexpr int SYRK_STAGES = 4;    // LDS ring depth (16 KB a stage; deeper rings measured no faster)
 constexpr int PANEL = ST * 64;    // bytes per panel
 
 int syrk_tiles(int L) {
@@ -59,12 +59,25 @@ __device__ inline void wait_vmcnt() {
   __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
 }
 
-template <class T>
+// Wait for the oldest stage when `younger` (0..Y) later stages of LDPS loads each may stay
+// in flight (the count has to be an immediate).
+template <int LDPS, int Y>
+__device__ inline void wait_oldest_stage(int younger) {
+  if constexpr (Y == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (younger >= Y) wait_vmcnt<Y * LDPS>();
+    else wait_oldest_stage<LDPS, Y - 1>(younger);
+  }
+}
+
+template <class T, int STAGES>
 __global__ __launch_bounds__(256) void syrk_kernel(const T* __restrict__ X, int B, int L, int C, int nsplit,
                                                    const T* __restrict__ zpad, float* __restrict__ part) {
   typedef MM<T> mm;
   typedef typename mm::frag frag;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[SYRK_STAGES][2][PANEL];
+  static_assert(STAGES >= 2 && 4 * (STAGES - 2) <= 63, "outstanding loads must fit the vmcnt counter");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES][2][PANEL];
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1);
   const int wave = tid / WAVE;
@@ -123,28 +136,21 @@ __global__ __launch_bounds__(256) void syrk_kernel(const T* __restrict__ X, int 
     for (int u = 0; u < 4; ++u) acc[t][u] = zero4();
 
 #pragma unroll
-  for (int st = 0; st < SYRK_STAGES - 1; ++st)
+  for (int st = 0; st < STAGES - 1; ++st)
     if (st < nq) issue(beg + st, st);
   const int g = lane >> 4;  // this lane's k-group
   for (int i = 0; i < nq; ++i) {
     // stage i has landed once at most the loads of the younger stages are outstanding
-    const int younger = (nq - 1 - i) < (SYRK_STAGES - 2) ? (nq - 1 - i) : (SYRK_STAGES - 2);
-    if (diag) {
-      if (younger >= 2) wait_vmcnt<4>();
-      else if (younger == 1) wait_vmcnt<2>();
-      else wait_vmcnt<0>();
-    } else {
-      if (younger >= 2) wait_vmcnt<8>();
-      else if (younger == 1) wait_vmcnt<4>();
-      else wait_vmcnt<0>();
-    }
+    const int younger = (nq - 1 - i) < (STAGES - 2) ? (nq - 1 - i) : (STAGES - 2);
+    if (diag) wait_oldest_stage<2, STAGES - 2>(younger);
+    else wait_oldest_stage<4, STAGES - 2>(younger);
     // Bare s_barrier: every wave has waited for its own loads of stage i above, and a
     // __syncthreads fence would also drain the younger stages still in flight.
     bare_barrier();
     // the stage read last iteration is free again: refill it
-    if (i + SYRK_STAGES - 1 < nq) issue(beg + i + SYRK_STAGES - 1, (i + SYRK_STAGES - 1) % SYRK_STAGES);
-    const unsigned char* pa = lds[i % SYRK_STAGES][0];
-    const unsigned char* pb = diag ? pa : lds[i % SYRK_STAGES][1];
+    if (i + STAGES - 1 < nq) issue(beg + i + STAGES - 1, (i + STAGES - 1) % STAGES);
+    const unsigned char* pa = lds[i % STAGES][0];
+    const unsigned char* pb = diag ? pa : lds[i % STAGES][1];
     frag af[4], bf[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -204,7 +210,8 @@ template <class T>
 static hipError_t syrk_t(const void* X, int B, int L, int C, int nsplit, const void* zpad, float* part,
                          hipStream_t st) {
   dim3 grid(syrk_tiles(L) * nsplit);
-  hipLaunchKernelGGL(syrk_kernel<T>, grid, dim3(256), 0, st, (const T*)X, B, L, C, nsplit, (const T*)zpad, part);
+  hipLaunchKernelGGL((syrk_kernel<T, SYRK_STAGES>), grid, dim3(256), 0, st, (const T*)X, B, L, C, nsplit,
+                     (const T*)zpad, part);
   return hipGetLastError();
 }
 
@@ -227,7 +234,8 @@ __global__ __launch_bounds__(256) void build_io_kernel(const float* __restrict__
                                                        const int* __restrict__ dRx, const int* __restrict__ dRy,
                                                        int L, int ldL, int R_max, T* __restrict__ PQ,
                                                        T* __restrict__ Qt, int ldQt) {
-  const int Rx = *dRx, Ry = *dRy;
+  // ranks outside [0, R_max] come from a failed truncation; the copies are then unused
+  const int Rx = min(max(*dRx, 0), R_max), Ry = min(max(*dRy, 0), R_max);
   const size_t n1 = (size_t)2 * R_max * ldL;
   const size_t n2 = (size_t)L * ldQt;
   for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n1 + n2; e += (size_t)gridDim.x * 256) {

@@ -66,12 +66,13 @@ constexpr int F_SCALE = 12;     // 2 doubles: ||C||_F^2 per side
 constexpr int F_BARRIER = 16;   // sweep barrier arrivals
 constexpr int F_ABORT = 17;     // a bounded wait timed out
 constexpr int F_NALIVE = 18;    // [2] columns above the noise floor
+constexpr int F_INFO = 24;      // [2][INFO_WORDS] copy of each side's info block
 constexpr size_t EIG_FLAGS_BYTES = 256;
 
 struct EigBufs {
   float* W[2];
-  float* Wtmp;      // statistic in float32 before the warm start product
-  float* V32;       // the accumulated rotation in float32, for that product
+  float* Wtmp[2];   // statistic in float32 before the warm start product
+  float* V32[2];    // the accumulated rotation in float32, for that product
   double* V[2];
   float* nrm[2];
   int* flags;
@@ -86,10 +87,14 @@ static EigBufs eig_bufs(void* work, const EigLayout& e) {
   p += e.wbytes;
   b.W[1] = (float*)p;
   p += e.wbytes;
-  b.Wtmp = (float*)p;
-  p += e.wbytes;
-  b.V32 = (float*)p;
-  p += e.wbytes;
+  for (int s = 0; s < 2; ++s) {
+    b.Wtmp[s] = (float*)p;
+    p += e.wbytes;
+  }
+  for (int s = 0; s < 2; ++s) {
+    b.V32[s] = (float*)p;
+    p += e.wbytes;
+  }
   b.V[0] = (double*)p;
   p += e.vbytes;
   b.V[1] = (double*)p;
@@ -110,22 +115,35 @@ static EigBufs eig_bufs(void* work, const EigLayout& e) {
 
 size_t eig_workspace_bytes(int L) {
   const EigLayout e = eig_layout(L);
-  return 4 * e.wbytes + 2 * e.vbytes + 2 * e.nrmbytes + EIG_FLAGS_BYTES + e.verbytes + 2 * e.colbytes;
+  return 6 * e.wbytes + 2 * e.vbytes + 2 * e.nrmbytes + EIG_FLAGS_BYTES + e.verbytes + 2 * e.colbytes;
 }
 
 // ---------------------------------------------------------------------------- set-up kernels
+// The set-up and read-out kernels treat both statistics in one launch: blockIdx.y (or
+// blockIdx.x for the one-block kernels) selects the side, 0 = C_X, 1 = C_G.
+struct EigSides {
+  const double* S[2];  // statistic sums (upper triangle, row-major L x L)
+  double inv[2];       // 1 / samples
+  float* Wp[2];        // where the prep kernel writes C (W cold, the staging copy warm)
+  float* W[2];
+  double* V[2];
+  float* V32[2];
+  float* nrm[2];
+  int* cols[2];
+};
 
 // W[c][r] = S[min(r,c)][max(r,c)] * inv_n (column-major, zero padding); flags non-finite sums.
-__global__ __launch_bounds__(256) void jacobi_prep_kernel(const double* __restrict__ S, double inv_n, int L, int ldw,
-                                                          float* __restrict__ W, int* __restrict__ bad) {
-  const int c = blockIdx.x;
+__global__ __launch_bounds__(256) void jacobi_prep_kernel(EigSides a, int L, int ldw, int* __restrict__ bad) {
+  const int c = blockIdx.x, s = blockIdx.y;
+  const double* S = a.S[s];
+  float* W = a.Wp[s];
   for (int r = threadIdx.x; r < ldw; r += 256) {
     float v = 0.0f;
     if (r < L && c < L) {
       const int i = r < c ? r : c;
       const int j = r < c ? c : r;
-      const double d = S[(size_t)i * L + j] * inv_n;
-      if (!isfinite(d)) atomicOr(bad, 1);
+      const double d = S[(size_t)i * L + j] * a.inv[s];
+      if (!isfinite(d)) atomicOr(bad + s, 1);
       v = (float)d;
     }
     W[(size_t)c * ldw + r] = v;
@@ -133,22 +151,25 @@ __global__ __launch_bounds__(256) void jacobi_prep_kernel(const double* __restri
 }
 
 // V = I (column-major, ncols x ldw).
-__global__ __launch_bounds__(256) void identity_kernel(double* __restrict__ V, int ldw) {
+__global__ __launch_bounds__(256) void identity_kernel(EigSides a, int ldw) {
   const int c = blockIdx.x;
+  double* V = a.V[blockIdx.y];
   for (int r = threadIdx.x; r < ldw; r += 256) V[(size_t)c * ldw + r] = (r == c) ? 1.0 : 0.0;
 }
 
 // Warm start, step 1: the accumulated rotation rounded to float32 (column-major, as stored).
 // Rounding V here only perturbs W = C V at float32 resolution; the rotation itself stays
 // float64.
-__global__ __launch_bounds__(256) void v_to_f32_kernel(const double* __restrict__ V, size_t n, float* __restrict__ V32) {
+__global__ __launch_bounds__(256) void v_to_f32_kernel(EigSides a, size_t n) {
+  const double* V = a.V[blockIdx.y];
+  float* V32 = a.V32[blockIdx.y];
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) V32[i] = (float)V[i];
 }
 
 // Column norms of W: sigma_c = ||W[:, c]||, c < L.
-__global__ __launch_bounds__(64) void colnorm_kernel(const float* __restrict__ W, int ldw, int L,
-                                                     float* __restrict__ nrm) {
+__global__ __launch_bounds__(64) void colnorm_kernel(EigSides a, int ldw, int L) {
   const int c = blockIdx.x;
+  const float* W = a.W[blockIdx.y];
   const int lane = threadIdx.x;
   float acc = 0.0f;
   for (int r = lane; r < L; r += 64) {
@@ -156,33 +177,36 @@ __global__ __launch_bounds__(64) void colnorm_kernel(const float* __restrict__ W
     acc += v * v;
   }
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) nrm[c] = sqrtf(acc);
+  if (lane == 0) a.nrm[blockIdx.y][c] = sqrtf(acc);
 }
 
-// ||W||_F^2 from the column norms, in a fixed order (one block).
-__global__ __launch_bounds__(256) void frob_kernel(const float* __restrict__ nrm, int L, double* __restrict__ out) {
-  __shared__ double red[256];
-  double acc = 0.0;
-  for (int c = threadIdx.x; c < L; c += 256) acc += (double)nrm[c] * (double)nrm[c];
-  red[threadIdx.x] = acc;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) *out = red[0];
-}
-
-// Deflation: columns whose squared norm is under the noise floor are left out of the
-// tournament (they would never be rotated). cols = [columns above the floor in index
-// order, then the others]; n_alive counts the first group. One block.
-__global__ __launch_bounds__(1024) void alive_kernel(const float* __restrict__ nrm, const double* __restrict__ scale,
-                                                     int L, int ncols, int* __restrict__ cols,
-                                                     int* __restrict__ n_alive) {
+// ||W||_F^2 from the column norms in a fixed order, then deflation: columns whose squared
+// norm is under the noise floor are left out of the tournament (they would never be
+// rotated). cols = [columns above the floor in index order, then the others]; n_alive
+// counts the first group. One block of 1024 threads per side (blockIdx.x), ncols <= 2048.
+__global__ __launch_bounds__(1024) void frob_alive_kernel(EigSides a, double* __restrict__ scale_out, int L,
+                                                          int ncols, int* __restrict__ n_alive_out) {
   __shared__ int flag[2048];
   __shared__ int sum[1024];
-  const double floor_g = NOISE_REL * *scale;
+  __shared__ double fro[1024];
+  const int side = blockIdx.x;
+  const float* nrm = a.nrm[side];
+  int* cols = a.cols[side];
+  int* n_alive = n_alive_out + side;
   const int tid = threadIdx.x;
+  {
+    double acc = 0.0;
+    for (int c = tid; c < L; c += 1024) acc += (double)nrm[c] * (double)nrm[c];
+    fro[tid] = acc;
+    __syncthreads();
+    for (int st = 512; st > 0; st >>= 1) {
+      if (tid < st) fro[tid] += fro[tid + st];
+      __syncthreads();
+    }
+  }
+  const double scale = fro[0];
+  if (tid == 0) scale_out[side] = scale;
+  const double floor_g = NOISE_REL * scale;
   // two columns per thread (ncols <= 2048)
   int f[2], own = 0;
 #pragma unroll
@@ -241,11 +265,9 @@ struct JacobiArgs {
 
 struct JacobiSmem {
   int col[16];
-  int partner[16];
   float part[4][16][17];
   double G[16][17];
   double V[16][17];
-  double jd[16], jo[16];
   int need;
   int ok;
 };
@@ -345,61 +367,52 @@ __device__ void jacobi_pair(const JacobiArgs& a, int side, int ba, int bb, int s
     }
     wave_lds_sync();
 
-    // Inner cyclic Jacobi, at most two sweeps per visit. Angles come from float32
-    // arithmetic; each (c, s) is renormalised in float64 so that every accumulated
-    // rotation is orthogonal to float64 precision.
+    // Inner cyclic Jacobi, at most two sweeps per visit, in circle-method order: in step ir
+    // the 16 indices form 8 disjoint pairs, and lane (a, b) = (lane / 8, lane % 8) owns the
+    // 2x2 block rows(pair a) x cols(pair b), which the step updates on its own:
+    // G <- J_a^T G J_b, V <- V J_b. The diagonal lanes (a == b) hold their pair's 2x2 and
+    // choose its rotation. Angles come from float32 arithmetic; each (c, s) is
+    // renormalised in float64 so that every accumulated rotation is orthogonal to float64
+    // precision.
+    const int pa = lane >> 3, pb = lane & 7;
+    const double rt2 = (double)a.rot_tol * (double)a.rot_tol;
     for (int isweep = 0; isweep < 2 && sm.need; ++isweep) {
       int rotated = 0;
       for (int ir = 0; ir < 15; ++ir) {
-        if (lane < 8) {
-          const int p = tourney(lane, ir, 16);
-          const int q = tourney(15 - lane, ir, 16);
-          const double ad = sm.G[p][p], dd = sm.G[q][q], od = sm.G[p][q];
-          double c = 1.0, sn = 0.0;
-          if (ad > floor_g && dd > floor_g && fabs(od) > (double)a.rot_tol * sqrt(ad * dd)) {
-            const float zeta = (float)((dd - ad) / (2.0 * od));
-            const float t = copysignf(1.0f, zeta) / (fabsf(zeta) + sqrtf(1.0f + zeta * zeta));
-            const float cf = rsqrtf(1.0f + t * t);
-            c = (double)cf;
-            sn = (double)(t * cf);
-            const double dlt = c * c + sn * sn - 1.0;  // |dlt| ~ 1e-7
-            const double nrm = 1.0 - 0.5 * dlt + 0.375 * dlt * dlt;
-            c *= nrm;
-            sn *= nrm;
-            rotated = 1;
-          }
-          // new column p = c*p - s*q, new column q = s*p + c*q
-          sm.partner[p] = q;
-          sm.jd[p] = c;
-          sm.jo[p] = -sn;
-          sm.partner[q] = p;
-          sm.jd[q] = c;
-          sm.jo[q] = sn;
+        const int r0 = tourney(pa, ir, 16), r1 = tourney(15 - pa, ir, 16);
+        const int c0 = tourney(pb, ir, 16), c1 = tourney(15 - pb, ir, 16);
+        const double g00 = sm.G[r0][c0], g01 = sm.G[r0][c1], g10 = sm.G[r1][c0], g11 = sm.G[r1][c1];
+        const double v00 = sm.V[r0][c0], v01 = sm.V[r0][c1], v10 = sm.V[r1][c0], v11 = sm.V[r1][c1];
+        double c = 1.0, sn = 0.0;
+        if (pa == pb && g00 > floor_g && g11 > floor_g && g01 * g01 > rt2 * g00 * g11) {
+          // rotate the pair (p, q) = (r0, r1): new p = c p - s q, new q = s p + c q
+          const float zeta = (float)((g11 - g00) * 0.5 * __builtin_amdgcn_rcp(g01));
+          const float t = copysignf(1.0f, zeta) / (fabsf(zeta) + sqrtf(1.0f + zeta * zeta));
+          const float cf = rsqrtf(1.0f + t * t);
+          c = (double)cf;
+          sn = (double)(t * cf);
+          const double dlt = c * c + sn * sn - 1.0;  // |dlt| ~ 1e-7
+          const double nrm = 1.0 - 0.5 * dlt + 0.375 * dlt * dlt;
+          c *= nrm;
+          sn *= nrm;
+          rotated = 1;
         }
-        wave_lds_sync();
-        double gn[4], vn[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int idx = lane * 4 + e;
-          const int x = idx >> 4, y = idx & 15;
-          const int ox = sm.partner[x], oy = sm.partner[y];
-          const double jdx = sm.jd[x], jox = sm.jo[x], jdy = sm.jd[y], joy = sm.jo[y];
-          gn[e] = jdx * (jdy * sm.G[x][y] + joy * sm.G[x][oy]) + jox * (jdy * sm.G[ox][y] + joy * sm.G[ox][oy]);
-          vn[e] = sm.V[x][y] * jdy + sm.V[x][oy] * joy;
-        }
-        wave_lds_sync();
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int idx = lane * 4 + e;
-          sm.G[idx >> 4][idx & 15] = gn[e];
-          sm.V[idx >> 4][idx & 15] = vn[e];
-        }
+        const double ca = __shfl(c, 9 * pa), sa = __shfl(sn, 9 * pa);
+        const double cb = __shfl(c, 9 * pb), sb = __shfl(sn, 9 * pb);
+        const double h00 = cb * g00 - sb * g01, h01 = sb * g00 + cb * g01;
+        const double h10 = cb * g10 - sb * g11, h11 = sb * g10 + cb * g11;
+        sm.G[r0][c0] = ca * h00 - sa * h10;
+        sm.G[r1][c0] = sa * h00 + ca * h10;
+        sm.G[r0][c1] = ca * h01 - sa * h11;
+        sm.G[r1][c1] = sa * h01 + ca * h11;
+        sm.V[r0][c0] = cb * v00 - sb * v01;
+        sm.V[r0][c1] = sb * v00 + cb * v01;
+        sm.V[r1][c0] = cb * v10 - sb * v11;
+        sm.V[r1][c1] = sb * v10 + cb * v11;
+        // the next step's blocks hold entries other lanes wrote in this one
         wave_lds_sync();
       }
-      // wave-uniform: every lane saw the same rotations
-      rotated = __shfl(rotated, 0) | __shfl(rotated, 1) | __shfl(rotated, 2) | __shfl(rotated, 3) |
-                __shfl(rotated, 4) | __shfl(rotated, 5) | __shfl(rotated, 6) | __shfl(rotated, 7);
-      if (!rotated) break;
+      if (__ballot(rotated) == 0) break;  // wave-uniform
     }
   }
   __syncthreads();
@@ -524,12 +537,25 @@ constexpr int INFO_STATUS = 0, INFO_K = 1, INFO_R = 2, INFO_C = 3, INFO_KEPT = 4
 
 // One block of 1024 threads: sort the L column norms (descending, ties by column index),
 // energy prefix in float64, truncation, compensation and P = c * U_R^T.
-__global__ __launch_bounds__(1024) void truncate_build_kernel(const float* __restrict__ W, int ldw, int L,
-                                                              const float* __restrict__ nrm, float eps, int p,
-                                                              int comp, int R_max, const int* __restrict__ bad,
-                                                              const int* __restrict__ converged,
-                                                              float* __restrict__ P32, float* __restrict__ sigma_out,
-                                                              int* __restrict__ info) {
+struct TruncArgs {
+  const float* W[2];
+  const float* nrm[2];
+  float* P32[2];
+  float* sigma[2];
+  int* info[2];
+  float eps;
+  int p, comp, R_max;
+};
+
+__global__ __launch_bounds__(1024) void truncate_build_kernel(TruncArgs a, int ldw, int L, int* __restrict__ flags) {
+  const int side = blockIdx.x;
+  const float* __restrict__ W = a.W[side];
+  const float* __restrict__ nrm = a.nrm[side];
+  float* __restrict__ P32 = a.P32[side];
+  float* __restrict__ sigma_out = a.sigma[side];
+  int* __restrict__ info = a.info[side];
+  const float eps = a.eps;
+  const int p = a.p, comp = a.comp, R_max = a.R_max;
   __shared__ float key[MAX_L];
   __shared__ int idx[MAX_L];
   __shared__ double prefix_last, prefix_k, prefix_R;
@@ -568,8 +594,8 @@ __global__ __launch_bounds__(1024) void truncate_build_kernel(const float* __res
 
   if (tid == 0) {
     int status = 0;
-    if (*bad) status = 6;            // non-finite statistics
-    else if (!*converged) status = 7;  // no convergence
+    if (flags[F_BAD + side]) status = 6;        // non-finite statistics
+    else if (!flags[F_CONV + side]) status = 7;  // no convergence
     // ordered float64 prefix of sigma^2
     double run = 0.0;
     for (int i = 0; i < L; ++i) {
@@ -655,14 +681,18 @@ __global__ __launch_bounds__(1024) void truncate_build_kernel(const float* __res
     }
   }
   if (tid == 0) {
-    info[INFO_STATUS] = sstatus;
-    info[INFO_K] = sk;
-    info[INFO_R] = sR;
-    info[INFO_C] = __float_as_int(sc);
+    // the info block goes to the caller's buffer and to the flags, which the host reads
+    int* dst[2] = {info, flags + F_INFO + INFO_WORDS * side};
     const double kept = prefix_last > 0.0 ? prefix_R / prefix_last : 0.0;
     const double keptk = prefix_last > 0.0 ? prefix_k / prefix_last : 0.0;
-    *reinterpret_cast<double*>(info + INFO_KEPT) = kept;
-    *reinterpret_cast<double*>(info + INFO_KEPTK) = keptk;
+    for (int d = 0; d < 2; ++d) {
+      dst[d][INFO_STATUS] = sstatus;
+      dst[d][INFO_K] = sk;
+      dst[d][INFO_R] = sR;
+      dst[d][INFO_C] = __float_as_int(sc);
+      __builtin_memcpy(dst[d] + INFO_KEPT, &kept, 8);
+      __builtin_memcpy(dst[d] + INFO_KEPTK, &keptk, 8);
+    }
   }
 }
 
@@ -678,30 +708,35 @@ hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv
   double* scale = (double*)(flags + F_SCALE);
   hipError_t err;
   if ((err = launch_zero(flags, EIG_FLAGS_BYTES + e.verbytes, st)) != hipSuccess) return err;
-  const double* S[2] = {SX, SG};
-  const double inv[2] = {inv_nx, inv_ng};
+  EigSides sd;
+  sd.S[0] = SX;
+  sd.S[1] = SG;
+  sd.inv[0] = inv_nx;
+  sd.inv[1] = inv_ng;
   for (int s = 0; s < 2; ++s) {
-    if (warm) {
-      hipLaunchKernelGGL(jacobi_prep_kernel, dim3(e.ncols), dim3(256), 0, st, S[s], inv[s], L, e.ldw, b.Wtmp,
-                         flags + F_BAD + s);
-      // W[c][r] = sum_k V[k][c] C[k][r]: A = V^T stored [ncols][ldw] (k contiguous), B = C
-      // stored [k][r] (r contiguous), both float32, on the matrix cores
-      const size_t nv = (size_t)e.ncols * e.ldw;
-      hipLaunchKernelGGL(v_to_f32_kernel, dim3((unsigned)std::min<size_t>((nv + 255) / 256, 2048)), dim3(256), 0, st,
-                         b.V[s], nv, b.V32);
-      if ((err = launch_gemm(false, false, b.V32, e.ldw, 0, b.Wtmp, e.ldw, 0, b.W[s], e.ldw, 0, 1, e.ncols, e.ldw, L,
-                             st)) != hipSuccess)
-        return err;
-    } else {
-      hipLaunchKernelGGL(jacobi_prep_kernel, dim3(e.ncols), dim3(256), 0, st, S[s], inv[s], L, e.ldw, b.W[s],
-                         flags + F_BAD + s);
-      hipLaunchKernelGGL(identity_kernel, dim3(e.ncols), dim3(256), 0, st, b.V[s], e.ldw);
-    }
-    hipLaunchKernelGGL(colnorm_kernel, dim3(L), dim3(64), 0, st, b.W[s], e.ldw, L, b.nrm[s]);
-    hipLaunchKernelGGL(frob_kernel, dim3(1), dim3(256), 0, st, b.nrm[s], L, scale + s);
-    hipLaunchKernelGGL(alive_kernel, dim3(1), dim3(1024), 0, st, b.nrm[s], scale + s, L, e.ncols, b.cols[s],
-                       flags + F_NALIVE + s);
+    sd.Wp[s] = warm ? b.Wtmp[s] : b.W[s];
+    sd.W[s] = b.W[s];
+    sd.V[s] = b.V[s];
+    sd.V32[s] = b.V32[s];
+    sd.nrm[s] = b.nrm[s];
+    sd.cols[s] = b.cols[s];
   }
+  hipLaunchKernelGGL(jacobi_prep_kernel, dim3(e.ncols, 2), dim3(256), 0, st, sd, L, e.ldw, flags + F_BAD);
+  if (warm) {
+    // W[c][r] = sum_k V[k][c] C[k][r]: A = V^T stored [ncols][ldw] (k contiguous), B = C
+    // stored [k][r] (r contiguous), both float32, on the matrix cores; one batch per side
+    const size_t nv = (size_t)e.ncols * e.ldw;
+    hipLaunchKernelGGL(v_to_f32_kernel, dim3((unsigned)std::min<size_t>((nv + 255) / 256, 1024), 2), dim3(256), 0, st,
+                       sd, nv);
+    if ((err = launch_gemm(false, false, b.V32[0], e.ldw, (size_t)(b.V32[1] - b.V32[0]), b.Wtmp[0], e.ldw,
+                           (size_t)(b.Wtmp[1] - b.Wtmp[0]), b.W[0], e.ldw, (size_t)(b.W[1] - b.W[0]), 2, e.ncols,
+                           e.ldw, L, st)) != hipSuccess)
+      return err;
+  } else {
+    hipLaunchKernelGGL(identity_kernel, dim3(e.ncols, 2), dim3(256), 0, st, sd, e.ldw);
+  }
+  hipLaunchKernelGGL(colnorm_kernel, dim3(L, 2), dim3(64), 0, st, sd, e.ldw, L);
+  hipLaunchKernelGGL(frob_alive_kernel, dim3(2), dim3(1024), 0, st, sd, scale, L, e.ncols, flags + F_NALIVE);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   JacobiArgs ja;
@@ -730,15 +765,26 @@ hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv
   err = hipLaunchCooperativeKernel((const void*)jacobi_kernel, dim3(e.nb), dim3(256), kargs, dyn, st);
   if (err != hipSuccess) return err;
 
-  float* P[2] = {out.P32, out.Q32};
-  float* sig[2] = {out.sigma_x, out.sigma_g};
-  int* info[2] = {out.info_x, out.info_g};
+  hipLaunchKernelGGL(colnorm_kernel, dim3(L, 2), dim3(64), 0, st, sd, e.ldw, L);
+  TruncArgs ta;
   for (int s = 0; s < 2; ++s) {
-    hipLaunchKernelGGL(colnorm_kernel, dim3(L), dim3(64), 0, st, b.W[s], e.ldw, L, b.nrm[s]);
-    hipLaunchKernelGGL(truncate_build_kernel, dim3(1), dim3(1024), 0, st, b.W[s], e.ldw, L, b.nrm[s], out.eps, out.p,
-                       out.comp, out.R_max, flags + F_BAD + s, flags + F_CONV + s, P[s], sig[s], info[s]);
+    ta.W[s] = b.W[s];
+    ta.nrm[s] = b.nrm[s];
   }
+  ta.P32[0] = out.P32;
+  ta.P32[1] = out.Q32;
+  ta.sigma[0] = out.sigma_x;
+  ta.sigma[1] = out.sigma_g;
+  ta.info[0] = out.info_x;
+  ta.info[1] = out.info_g;
+  ta.eps = out.eps;
+  ta.p = out.p;
+  ta.comp = out.comp;
+  ta.R_max = out.R_max;
+  hipLaunchKernelGGL(truncate_build_kernel, dim3(2), dim3(1024), 0, st, ta, e.ldw, L, flags);
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  // work that depends on the outcome is queued by the caller before this read-back
+  if (out.before_readback && (err = out.before_readback(out.ctx, st)) != hipSuccess) return err;
   if ((err = hipMemcpyAsync(host_flags, flags, EIG_HOST_FLAGS * sizeof(int), hipMemcpyDeviceToHost, st)) != hipSuccess)
     return err;
   if ((err = hipStreamSynchronize(st)) != hipSuccess) return err;

@@ -7,6 +7,8 @@
 //           g_hat_x = (Q gy) w               (contraction over K = Cy)
 //   expand  g_x_b = Q^T g_hat_x_b            (contraction over K = Ry)
 // All contractions run on the matrix cores with float32 accumulation.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -300,8 +302,8 @@ struct GxShared {
 template <class T, int MTA, int KS, int NW>
 __device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const T* __restrict__ w,
                                                const T* __restrict__ At, int ldA, int R, int L, int Cy, int Cx,
-                                               T* __restrict__ out, int strip, int b, float (*red)[8][4][WAVE],
-                                               GxShared<T, KS>& gs) {
+                                               T* __restrict__ out, int strip, int b, int z, int nz,
+                                               float (*red)[8][4][WAVE], GxShared<T, KS>& gs) {
   typedef MM<T> mm;
   typedef typename mm::frag frag;
   constexpr int U = 2;
@@ -367,24 +369,29 @@ __device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const 
     __syncthreads();
   }
 
-  // phase 2: expand over all tokens; each wave takes every NW-th 16-token tile
+  // phase 2: expand over this block's share of the tokens (16-token tiles [t_beg, t_end));
+  // each wave takes every NW-th tile
   frag bz[KS][8];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) load_strip_T<T, 8>(&gsm[0][0], 128, ks * mm::KSTEP + kl, R, lc, true, bz[ks]);
   constexpr int MPW = 4;
   const int ntl = (L + 15) / 16;
-  for (int tl0 = wave; tl0 < ntl; tl0 += NW * MPW) {
+  const int t_beg = (int)((long)ntl * z / nz), t_end = (int)((long)ntl * (z + 1) / nz);
+  for (int tl0 = t_beg + wave; tl0 < t_end; tl0 += NW * MPW) {
     frag af[MPW][KS];
 #pragma unroll
     for (int i = 0; i < MPW; ++i) {
-      const int la = 16 * (tl0 + i * NW) + (lane & 15);
+      const int tl = tl0 + i * NW;
+      const int la = 16 * tl + (lane & 15);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) af[i][ks] = load_frag<T>(At + (size_t)la * ldA + ks * mm::KSTEP + kl, la < L);
+      for (int ks = 0; ks < KS; ++ks)
+        af[i][ks] = load_frag<T>(At + (size_t)la * ldA + ks * mm::KSTEP + kl, tl < t_end && la < L);
     }
 #pragma unroll
     for (int i = 0; i < MPW; ++i) {
-      const int l0 = 16 * (tl0 + i * NW);
-      if (l0 >= L) break;
+      const int tl = tl0 + i * NW;
+      if (tl >= t_end) break;
+      const int l0 = 16 * tl;
       f32x4 o4[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) o4[j] = zero4();
@@ -408,31 +415,24 @@ __device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const 
   }
 }
 
-template <class T, int MTA, int KS, int NW>
-__global__ __launch_bounds__(NW * WAVE) void gx_fused_kernel(const T* __restrict__ Qgy, const T* __restrict__ w,
-                                                             const T* __restrict__ At, int ldA, int R, int L,
-                                                             int Cy, int Cx, T* __restrict__ out) {
-  __shared__ float red[NW][8][4][WAVE];
-  __shared__ __attribute__((aligned(16))) GxShared<T, KS> gs;
-  gx_fused_block<T, MTA, KS, NW>(Qgy, w, At, ldA, R, L, Cy, Cx, out, blockIdx.x, blockIdx.y, red, gs);
-}
-
 // The fused g_x blocks and the g_w blocks in one launch: both depend only on the stacked
 // projection, and the g_w tiles fill the compute units the g_x strips leave free.
-// Blocks [0, ngx) are g_x (strip = id % nstrip, sample = id / nstrip); the rest are g_w
-// tiles (64 x 128, K split over the NW waves).
+// Blocks [0, ngx) are g_x (strip = id % nstrip, then token chunk z < nz, then sample);
+// the rest are g_w tiles (64 x 128, K split over the NW waves).
 template <class T, int MTA, int KS, int NW>
 __global__ __launch_bounds__(NW * WAVE) void bwd_tail_kernel(const T* __restrict__ Qgy, const T* __restrict__ w,
                                                              const T* __restrict__ At, int ldA, int R, int L,
                                                              int Cy, int Cx, T* __restrict__ gx, int nstrip,
-                                                             int ngx, const T* __restrict__ Pgy,
+                                                             int nz, int ngx, const T* __restrict__ Pgy,
                                                              const T* __restrict__ xhat, T* __restrict__ gw,
                                                              int Kw, int gw_bx) {
   __shared__ float red[NW][8][4][WAVE];
   __shared__ __attribute__((aligned(16))) GxShared<T, KS> gs;
   const int id = blockIdx.x;
   if (id < ngx) {
-    gx_fused_block<T, MTA, KS, NW>(Qgy, w, At, ldA, R, L, Cy, Cx, gx, id % nstrip, id / nstrip, red, gs);
+    const int rest = id / nstrip;
+    gx_fused_block<T, MTA, KS, NW>(Qgy, w, At, ldA, R, L, Cy, Cx, gx, id % nstrip, rest / nz, rest % nz, nz, red,
+                                   gs);
   } else {
     // g_w = sum_b (P gy_b)^T x_hat_b: M = Cy, N = Cx, K = B*Rx (A stored [K][Cy])
     const int t = id - ngx;
@@ -560,42 +560,19 @@ hipError_t launch_expand(bool bf16_io, const void* At, int ldA, const void* Bz, 
 }
 
 template <class T, int MTA, int KS>
-static hipError_t gx_fused_cfg(const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L, int Cy,
-                               int Cx, void* out, hipStream_t st) {
-  constexpr int NW = MTA == 1 ? 8 : 4;  // 512-thread blocks only where the registers fit
-  dim3 grid((Cx + 127) / 128, B);
-  hipLaunchKernelGGL((gx_fused_kernel<T, MTA, KS, NW>), grid, dim3(NW * WAVE), 0, st, (const T*)Qgy, (const T*)w,
-                     (const T*)At, ldA, R, L, Cy, Cx, (T*)out);
-  return hipGetLastError();
-}
-
-template <class T>
-static hipError_t gx_fused_t(const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L, int Cy,
-                             int Cx, void* out, hipStream_t st) {
-  const int mta = (R + 15) / 16;
-  const int ks = (R + MM<T>::KSTEP - 1) / MM<T>::KSTEP;
-#define GXF(MA, K)                                                                        \
-  if (mta == MA && ks == K) return gx_fused_cfg<T, MA, K>(Qgy, w, At, ldA, B, R, L, Cy, Cx, out, st);
-  if constexpr (MM<T>::KSTEP == 32) {
-    GXF(1, 1) GXF(2, 1) GXF(3, 2) GXF(4, 2)
-  } else {
-    GXF(1, 1) GXF(2, 2) GXF(3, 3) GXF(4, 4)
-  }
-#undef GXF
-  return hipErrorInvalidValue;
-}
-
-template <class T, int MTA, int KS>
 static hipError_t bwd_tail_cfg(const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L, int Cy,
                                int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw,
                                hipStream_t st) {
   constexpr int NW = MTA == 1 ? 8 : 4;
   const int nstrip = (Cx + 127) / 128;
-  const int ngx = nstrip * B;
+  // one token chunk per sample: each further chunk repeats the g_hat_x phase, whose read
+  // of the w strip costs more than the extra parallelism gains
+  const int nz = 1;
+  const int ngx = nstrip * B * nz;
   const int gw_bx = (Cx + 127) / 128, gw_by = (Cy + 63) / 64;
   hipLaunchKernelGGL((bwd_tail_kernel<T, MTA, KS, NW>), dim3(ngx + gw_bx * gw_by), dim3(NW * WAVE), 0, st,
-                     (const T*)Qgy, (const T*)w, (const T*)At, ldA, R, L, Cy, Cx, (T*)gx, nstrip, ngx, (const T*)Pgy,
-                     (const T*)xhat, (T*)gw, Kw, gw_bx);
+                     (const T*)Qgy, (const T*)w, (const T*)At, ldA, R, L, Cy, Cx, (T*)gx, nstrip, nz, ngx,
+                     (const T*)Pgy, (const T*)xhat, (T*)gw, Kw, gw_bx);
   return hipGetLastError();
 }
 
@@ -625,12 +602,6 @@ hipError_t launch_bwd_tail(bool bf16_io, const void* Qgy, const void* w, const v
 bool gx_fused_applies(bool bf16_io, int B, int Cx, int Cy) {
   const double wbytes = (double)Cx * Cy * (bf16_io ? 2 : 4);
   return wbytes <= 2.0 * (1 << 20) && B * wbytes <= 64.0 * (1 << 20);
-}
-
-hipError_t launch_gx_fused(bool bf16_io, const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L,
-                           int Cy, int Cx, void* out, hipStream_t st) {
-  return bf16_io ? gx_fused_t<bf16>(Qgy, w, At, ldA, B, R, L, Cy, Cx, out, st)
-                 : gx_fused_t<float>(Qgy, w, At, ldA, B, R, L, Cy, Cx, out, st);
 }
 
 }  // namespace instant

@@ -23,14 +23,10 @@ hipError_t launch_gemm(bool bf16_io, bool a_trans, const void* A, int lda, size_
 hipError_t launch_expand(bool bf16_io, const void* At, int ldA, const void* Bz, int B, int R, int L, int C,
                          void* out, hipStream_t st);
 
-// gx[b][l][c] = sum_r At[l][r] (sum_k Qgy[b][r][k] w[k][c]) in one kernel, g_hat_x kept in
-// LDS (rounded to the I/O dtype). Applies when w is small enough to stay in L2.
+// gx[b][l][c] = sum_r At[l][r] (sum_k Qgy[b][r][k] w[k][c]) with g_hat_x kept in LDS
+// (rounded to the I/O dtype), and g_w = sum_b Pgy_b^T xhat_b (Pgy [Kw][Cy], xhat [Kw][Cx],
+// Kw = B * Rx), in one launch. Applies when w is small enough to stay in L2.
 bool gx_fused_applies(bool bf16_io, int B, int Cx, int Cy);
-hipError_t launch_gx_fused(bool bf16_io, const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L,
-                           int Cy, int Cx, void* out, hipStream_t st);
-
-// The fused g_x of launch_gx_fused and g_w = sum_b Pgy_b^T xhat_b (Pgy [Kw][Cy], xhat
-// [Kw][Cx], Kw = B * Rx) in one launch.
 hipError_t launch_bwd_tail(bool bf16_io, const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L,
                            int Cy, int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw,
                            hipStream_t st);
@@ -62,10 +58,14 @@ struct EigOut {
   float* sigma_g;
   int* info_x;
   int* info_g;
+  // optional: queued on the stream after the decomposition and before the host reads
+  // the flags back (the caller's follow-up work that needs no host decision)
+  hipError_t (*before_readback)(void* ctx, hipStream_t st) = nullptr;
+  void* ctx = nullptr;
 };
 constexpr int INFO_WORDS = 8;
-constexpr int EIG_HOST_FLAGS = 20;
-constexpr int EIGF_SWEEPS = 6, EIGF_CONV = 8, EIGF_BAD = 10, EIGF_NALIVE = 18;
+constexpr int EIG_HOST_FLAGS = 40;
+constexpr int EIGF_SWEEPS = 6, EIGF_CONV = 8, EIGF_BAD = 10, EIGF_NALIVE = 18, EIGF_INFO = 24;
 size_t eig_workspace_bytes(int L);
 int eig_max_L();
 hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv_ng, int L, int max_sweeps,
