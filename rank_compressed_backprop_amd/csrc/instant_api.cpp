@@ -118,11 +118,11 @@ inline instant_status hip_ok(hipError_t e) { return e == hipSuccess ? INSTANT_OK
 
 instant_status accumulate(instant_layer* h, const void* t, int B, int C, double* Sacc, hipStream_t st) {
   const int kstep = h->bf16 ? 32 : 16;
-  const int steps = (C + kstep - 1) / kstep;
-  const long total = (long)B * steps;
-  // slices of at least 32 k-steps (the LDS pipeline's fill is then small), enough of them
+  const int stages = ((C + kstep - 1) / kstep + 1) / 2;  // two k-steps per ring stage
+  const long total = (long)B * stages;
+  // slices of at least 16 stages (the LDS pipeline's fill is then small), enough of them
   // to give every compute unit a tile-slice, a multiple of 8 when there are 16 or more
-  int nsplit = (int)std::min<long>(syrk_split_cap(h->cfg.L), std::max<long>(1, total / 32));
+  int nsplit = (int)std::min<long>(syrk_split_cap(h->cfg.L), std::max<long>(1, total / 16));
   if (nsplit >= 16) nsplit -= nsplit % 8;
   hipError_t e = launch_syrk(h->bf16, t, B, h->cfg.L, C, nsplit, h->ws + h->lay.zpad, h->part(), st);
   if (e != hipSuccess) return INSTANT_E_HIP;

@@ -1,8 +1,8 @@
 // Calibration kernels of INSTANT (notes "INSTANT: Compressing Gradients and Activations
 // for Resource-Efficient Training", sections 关键设计 1 and 关键设计 2):
 //   syrk            running sums S += sum_b t_b t_b^T of the token autocorrelation, on the
-//                   matrix cores, upper-triangle 64x64 tiles, deterministic split reduction
-//                   into float64
+//                   matrix cores, upper-triangle 128x128 tiles, deterministic split
+//                   reduction into float64
 //   build_io        I/O-dtype copies of the published projections
 // The eigen-decomposition and truncation live in kernels_eig.hip.
 #include "common.hpp"
@@ -13,17 +13,17 @@ namespace instant {
 // ============================================================================ SYRK
 // Running sums S += sum_b X_b X_b^T over upper-triangle 128x128 tiles. A block of four
 // waves owns one tile and one slice of the (sample, channel) reduction; each wave owns a
-// 64x64 quarter. A k-step covers 64 bytes of every row (32 bf16 / 16 fp32 values); the
-// two row panels of a step (128 rows x 64 bytes each; one panel for diagonal tiles) go
-// straight from memory to LDS (global_load_lds, 16 bytes per lane) through an
-// SYRK_STAGES-deep ring, so several steps' loads are in flight while the matrix cores
-// consume the oldest. Within a panel, 16-byte chunk c of row r sits in slot
-// c ^ ((r >> 2) & 3), which makes the fragment reads bank-conflict-free. Lanes whose
-// row or channel is out of range read a zeroed pad instead. Slices write float32
-// partial tiles; a second kernel adds them to the float64 sums in slice order.
+// 64x64 quarter. A k-step covers 32 bf16 / 16 fp32 values; a stage of the LDS ring holds
+// two k-steps, i.e. 128 bytes (a whole cache line) of every row of the tile's two row
+// panels (one panel for diagonal tiles). Stages go straight from memory to LDS
+// (global_load_lds, 16 bytes per lane) through a SYRK_STAGES-deep ring, so later stages'
+// loads are in flight while the matrix cores consume the oldest. Within a panel, 16-byte
+// chunk c of row r sits in slot c ^ wide_swz(r), which keeps the fragment reads of 8 (and
+// of 16) consecutive rows on distinct banks. Lanes whose row or channel is out of range
+// read a zeroed pad instead. Slices write float32 partial tiles (in fragment order); a
+// second kernel adds them to the float64 sums in slice order.
 constexpr int ST = 128;           // statistics tile edge
-constexpr int SYRK_STAGES = 4;    // LDS ring depth (16 KB a stage; deeper rings measured no faster)
-constexpr int PANEL = ST * 64;    // bytes per panel
+constexpr int SYRK_STAGES = 3;    // LDS ring depth (32 KB a stage; deeper rings measured no faster)
 
 int syrk_tiles(int L) {
   const int T = (L + ST - 1) / ST;
@@ -71,20 +71,21 @@ __device__ inline void wait_oldest_stage(int younger) {
   }
 }
 
+constexpr int WPANEL = ST * 128;  // bytes per panel of a stage
+__device__ inline int wide_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 template <class T, int STAGES>
 __global__ __launch_bounds__(256) void syrk_kernel(const T* __restrict__ X, int B, int L, int C, int nsplit,
-                                                   const T* __restrict__ zpad, float* __restrict__ part) {
+                                                    const T* __restrict__ zpad, float* __restrict__ part) {
   typedef MM<T> mm;
   typedef typename mm::frag frag;
-  static_assert(STAGES >= 2 && 4 * (STAGES - 2) <= 63, "outstanding loads must fit the vmcnt counter");
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES][2][PANEL];
+  static_assert(STAGES >= 2 && 8 * (STAGES - 2) <= 63, "outstanding loads must fit the vmcnt counter");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES][2][WPANEL];
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1);
   const int wave = tid / WAVE;
   const int Tn = (L + ST - 1) / ST;
   const int ntiles = Tn * (Tn + 1) / 2;
-  // Workgroups are dealt to the 8 XCDs round-robin by linear id. With a multiple of 8
-  // slices, all tiles of a slice run on one XCD, so each sample is fetched into one L2.
   int tile, s;
   const int lin = blockIdx.x;
   if (nsplit % 8 == 0) {
@@ -99,27 +100,28 @@ __global__ __launch_bounds__(256) void syrk_kernel(const T* __restrict__ X, int 
   upper_tile(tile, Tn, ti, tj);
   const bool diag = ti == tj;
   const int steps_c = (C + mm::KSTEP - 1) / mm::KSTEP;
-  const int total = B * steps_c;
+  const int pairs_c = (steps_c + 1) / 2;
+  const int total = B * pairs_c;
   const int beg = (int)((long)total * s / nsplit);
   const int end = (int)((long)total * (s + 1) / nsplit);
   const int nq = end - beg;
 
-  // Each wave moves 1 KB of a panel per instruction: rows 16*j + lane/4 of wave-load j.
-  // Wave w issues wave-loads j = 2w, 2w+1 of each panel.
-  constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  // A slice is a range of stages in (sample, channel) order; a stage past the last channel
+  // reads zeros. Wave-load j = 4 * wave + h moves rows 8j .. 8j+7 of a panel (1 KB).
+  constexpr int EPC = 16 / (int)sizeof(T);
   auto issue = [&](int q, int stage) {
-    const int b = q / steps_c;
-    const int k0 = (q - b * steps_c) * mm::KSTEP;
+    const int b = q / pairs_c;
+    const int k0 = (q - b * pairs_c) * 2 * mm::KSTEP;
     const T* __restrict__ Xb = X + (size_t)b * L * C;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       if (p == 1 && diag) break;
       const int tb = p == 0 ? ti : tj;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int j = 2 * wave + h;
-        const int rloc = 16 * j + (lane >> 2);
-        const int chunk = (lane & 3) ^ ((rloc >> 2) & 3);
+      for (int h = 0; h < 4; ++h) {
+        const int j = 4 * wave + h;
+        const int rloc = 8 * j + (lane >> 3);
+        const int chunk = (lane & 7) ^ wide_swz(rloc);
         const int row = tb * ST + rloc;
         const int kk = k0 + chunk * EPC;
         const T* src = (row < L && kk < C) ? Xb + (size_t)row * C + kk : zpad;
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(256) void syrk_kernel(const T* __restrict__ X, int 
     }
   };
 
-  const int wr = wave >> 1, wc = wave & 1;  // this wave's 64x64 quarter
+  const int wr = wave >> 1, wc = wave & 1;
   f32x4 acc[4][4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -138,56 +140,52 @@ __global__ __launch_bounds__(256) void syrk_kernel(const T* __restrict__ X, int 
 #pragma unroll
   for (int st = 0; st < STAGES - 1; ++st)
     if (st < nq) issue(beg + st, st);
-  const int g = lane >> 4;  // this lane's k-group
+  const int g = lane >> 4;
   for (int i = 0; i < nq; ++i) {
-    // stage i has landed once at most the loads of the younger stages are outstanding
     const int younger = (nq - 1 - i) < (STAGES - 2) ? (nq - 1 - i) : (STAGES - 2);
-    if (diag) wait_oldest_stage<2, STAGES - 2>(younger);
-    else wait_oldest_stage<4, STAGES - 2>(younger);
-    // Bare s_barrier: every wave has waited for its own loads of stage i above, and a
-    // __syncthreads fence would also drain the younger stages still in flight.
+    if (diag) wait_oldest_stage<4, STAGES - 2>(younger);
+    else wait_oldest_stage<8, STAGES - 2>(younger);
     bare_barrier();
-    // the stage read last iteration is free again: refill it
     if (i + STAGES - 1 < nq) issue(beg + i + STAGES - 1, (i + STAGES - 1) % STAGES);
     const unsigned char* pa = lds[i % STAGES][0];
     const unsigned char* pb = diag ? pa : lds[i % STAGES][1];
-    frag af[4], bf[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int ra = 64 * wr + 16 * t + (lane & 15);
-      const int rb = 64 * wc + 16 * t + (lane & 15);
-      af[t] = *reinterpret_cast<const frag*>(pa + ra * 64 + 16 * (g ^ ((ra >> 2) & 3)));
-      bf[t] = *reinterpret_cast<const frag*>(pb + rb * 64 + 16 * (g ^ ((rb >> 2) & 3)));
+    for (int h = 0; h < 2; ++h) {
+      frag af[4], bf[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int ra = 64 * wr + 16 * t + (lane & 15);
+        const int rb = 64 * wc + 16 * t + (lane & 15);
+        af[t] = *reinterpret_cast<const frag*>(pa + ra * 128 + 16 * ((4 * h + g) ^ wide_swz(ra)));
+        bf[t] = *reinterpret_cast<const frag*>(pb + rb * 128 + 16 * ((4 * h + g) ^ wide_swz(rb)));
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[t][u] = mm::mma(af[t], bf[u], acc[t][u]);
     }
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) acc[t][u] = mm::mma(af[t], bf[u], acc[t][u]);
   }
 
+  // the partial tile in fragment order: one 16-byte store per lane and 16x16 tile
   float* __restrict__ out = part + ((size_t)s * ntiles + tile) * (ST * ST);
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = 64 * wr + 16 * t + 4 * (lane >> 4) + v;
-        const int col = 64 * wc + 16 * u + (lane & 15);
-        out[row * ST + col] = acc[t][u][v];
-      }
+      *reinterpret_cast<f32x4*>(out + (((wave * 16 + t * 4 + u) * WAVE + lane) * 4)) = acc[t][u];
 }
 
 // S[i][j] += sum_s part[s][tile] in split order, float64, for the upper-triangle tiles.
 __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restrict__ part, int nsplit, int ntiles,
                                                           int L, double* __restrict__ S) {
   const int tile = blockIdx.x;
-  const int e = blockIdx.y * 256 + threadIdx.x;
+  const int e = blockIdx.y * 256 + threadIdx.x;  // fragment-order index, see syrk_kernel
   const int Tn = (L + ST - 1) / ST;
   int ti, tj;
   upper_tile(tile, Tn, ti, tj);
-  const int i = ti * ST + e / ST;
-  const int j = tj * ST + e % ST;
+  const int wave = e >> 12, t = (e >> 10) & 3, u = (e >> 8) & 3, lane = (e >> 2) & 63, v = e & 3;
+  const int i = ti * ST + 64 * (wave >> 1) + 16 * t + 4 * (lane >> 4) + v;
+  const int j = tj * ST + 64 * (wave & 1) + 16 * u + (lane & 15);
   if (i >= L || j >= L) return;
   // independent loads, summed in split order
   const float* __restrict__ pp = part + (size_t)tile * (ST * ST) + e;

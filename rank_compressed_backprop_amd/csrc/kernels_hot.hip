@@ -306,7 +306,7 @@ __device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const 
                                                float (*red)[8][4][WAVE], GxShared<T, KS>& gs) {
   typedef MM<T> mm;
   typedef typename mm::frag frag;
-  constexpr int U = 2;
+  constexpr int U = 3;  // with 8 waves, the 24 k-steps of Cy = 768 in one round of loads
   constexpr int GROWS = GxShared<T, KS>::GROWS;
   auto& gsm = gs.g;
   const int lane = threadIdx.x & (WAVE - 1);
