@@ -289,51 +289,52 @@ __global__ __launch_bounds__(NW * WAVE) void expand_kernel(const T* __restrict__
 
 // ----------------------------------------------------------------------------- fused g_x
 // For layers whose weight stays resident in L2: block (strip, b) first forms
-// g_hat_x_b[:, strip] = Qgy_b (Ry x Cy) . w[:, strip] (Cy x 128) on the matrix cores
+// g_hat_x_b[:, strip] = Qgy_b (Ry x Cy) . w[:, strip] (Cy x 16*SW) on the matrix cores
 // (the NW waves split Cy, LDS sums them), keeps it in LDS in the I/O dtype, and then
-// expands g_x_b[:, strip] = Q^T g_hat_x_b[:, strip] over all L tokens.
-// Grid: (ceil(Cx / 128), B).
-template <class T, int KS>
+// expands g_x_b[:, strip] = Q^T g_hat_x_b[:, strip] over all L tokens. A lane owns SW
+// adjacent columns of the strip.
+template <class T, int KS, int SW>
 struct GxShared {
   static constexpr int GROWS = KS * MM<T>::KSTEP;  // rows of the LDS operand (zero beyond R)
-  T g[GROWS][128];
+  T g[GROWS][16 * SW];
 };
 
-template <class T, int MTA, int KS, int NW>
+template <class T, int MTA, int KS, int NW, int SW>
 __device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const T* __restrict__ w,
                                                const T* __restrict__ At, int ldA, int R, int L, int Cy, int Cx,
-                                               T* __restrict__ out, int strip, int b, int z, int nz,
-                                               float (*red)[8][4][WAVE], GxShared<T, KS>& gs) {
+                                               T* __restrict__ out, int strip, int b, float (*red)[SW][4][WAVE],
+                                               GxShared<T, KS, SW>& gs) {
   typedef MM<T> mm;
   typedef typename mm::frag frag;
   constexpr int U = 3;  // with 8 waves, the 24 k-steps of Cy = 768 in one round of loads
-  constexpr int GROWS = GxShared<T, KS>::GROWS;
+  constexpr int GROWS = GxShared<T, KS, SW>::GROWS;
+  constexpr int SC = 16 * SW;  // strip columns
   auto& gsm = gs.g;
   const int lane = threadIdx.x & (WAVE - 1);
   const int wave = threadIdx.x / WAVE;
-  const int lc = 8 * (lane & 15);  // column within the strip
-  const int col = strip * 128 + lc;
+  const int lc = SW * (lane & 15);  // column within the strip
+  const int col = strip * SC + lc;
   const bool col_ok = col < Cx;
   const int kl = mm::G * (lane >> 4);
   const T* __restrict__ Ab = Qgy + (size_t)b * R * Cy;
 
-  for (int e = threadIdx.x; e < GROWS * 128; e += NW * WAVE) (&gsm[0][0])[e] = (T)0.0f;
+  for (int e = threadIdx.x; e < GROWS * SC; e += NW * WAVE) (&gsm[0][0])[e] = (T)0.0f;
 
   // phase 1: g_hat_x tile
-  f32x4 acc[MTA][8];
+  f32x4 acc[MTA][SW];
 #pragma unroll
   for (int t = 0; t < MTA; ++t)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[t][j] = zero4();
+    for (int j = 0; j < SW; ++j) acc[t][j] = zero4();
   const int nsteps = (Cy + mm::KSTEP - 1) / mm::KSTEP;
   for (int s0 = wave; s0 < nsteps; s0 += NW * U) {
-    frag bf[U][8];
+    frag bf[U][SW];
     frag af[U][MTA];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = s0 + u * NW;
       const int k0 = s * mm::KSTEP + kl;
-      load_strip_T<T, 8>(w, Cx, k0, Cy, col, col_ok, bf[u]);
+      load_strip_T<T, SW>(w, Cx, k0, Cy, col, col_ok, bf[u]);
 #pragma unroll
       for (int t = 0; t < MTA; ++t) {
         const int m = 16 * t + (lane & 15);
@@ -345,12 +346,12 @@ __device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const 
 #pragma unroll
       for (int t = 0; t < MTA; ++t)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[t][j] = mm::mma(af[u][t], bf[u][j], acc[t][j]);
+        for (int j = 0; j < SW; ++j) acc[t][j] = mm::mma(af[u][t], bf[u][j], acc[t][j]);
   }
 #pragma unroll
   for (int t = 0; t < MTA; ++t) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < SW; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v) red[wave][j][v][lane] = acc[t][j][v];
     __syncthreads();
@@ -358,7 +359,7 @@ __device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const 
       const int r = 16 * t + 4 * (lane >> 4) + v;
       if (r < R) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < SW; ++j) {
           float sum = red[0][j][v][lane];
 #pragma unroll
           for (int ww = 1; ww < NW; ++ww) sum += red[ww][j][v][lane];
@@ -369,15 +370,13 @@ __device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const 
     __syncthreads();
   }
 
-  // phase 2: expand over this block's share of the tokens (16-token tiles [t_beg, t_end));
-  // each wave takes every NW-th tile
-  frag bz[KS][8];
+  // phase 2: expand over all tokens; each wave takes every NW-th 16-token tile
+  frag bz[KS][SW];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) load_strip_T<T, 8>(&gsm[0][0], 128, ks * mm::KSTEP + kl, R, lc, true, bz[ks]);
+  for (int ks = 0; ks < KS; ++ks) load_strip_T<T, SW>(&gsm[0][0], SC, ks * mm::KSTEP + kl, R, lc, true, bz[ks]);
   constexpr int MPW = 4;
   const int ntl = (L + 15) / 16;
-  const int t_beg = (int)((long)ntl * z / nz), t_end = (int)((long)ntl * (z + 1) / nz);
-  for (int tl0 = t_beg + wave; tl0 < t_end; tl0 += NW * MPW) {
+  for (int tl0 = wave; tl0 < ntl; tl0 += NW * MPW) {
     frag af[MPW][KS];
 #pragma unroll
     for (int i = 0; i < MPW; ++i) {
@@ -385,29 +384,29 @@ __device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const 
       const int la = 16 * tl + (lane & 15);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        af[i][ks] = load_frag<T>(At + (size_t)la * ldA + ks * mm::KSTEP + kl, tl < t_end && la < L);
+        af[i][ks] = load_frag<T>(At + (size_t)la * ldA + ks * mm::KSTEP + kl, tl < ntl && la < L);
     }
 #pragma unroll
     for (int i = 0; i < MPW; ++i) {
       const int tl = tl0 + i * NW;
-      if (tl >= t_end) break;
+      if (tl >= ntl) break;
       const int l0 = 16 * tl;
-      f32x4 o4[8];
+      f32x4 o4[SW];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) o4[j] = zero4();
+      for (int j = 0; j < SW; ++j) o4[j] = zero4();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o4[j] = mm::mma(af[i][ks], bz[ks][j], o4[j]);
+        for (int j = 0; j < SW; ++j) o4[j] = mm::mma(af[i][ks], bz[ks][j], o4[j]);
       if (col_ok) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int l = l0 + 4 * (lane >> 4) + v;
           if (l < L) {
-            float o[8];
+            float o[SW];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) o[j] = o4[j][v];
-            store_row<T, 8>(out + ((size_t)b * L + l) * Cx + col, o);
+            for (int j = 0; j < SW; ++j) o[j] = o4[j][v];
+            store_row<T, SW>(out + ((size_t)b * L + l) * Cx + col, o);
           }
         }
       }
@@ -417,22 +416,21 @@ __device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const 
 
 // The fused g_x blocks and the g_w blocks in one launch: both depend only on the stacked
 // projection, and the g_w tiles fill the compute units the g_x strips leave free.
-// Blocks [0, ngx) are g_x (strip = id % nstrip, then token chunk z < nz, then sample);
-// the rest are g_w tiles (64 x 128, K split over the NW waves).
-template <class T, int MTA, int KS, int NW>
+// Blocks [0, ngx) are g_x (strip = id % nstrip, sample = id / nstrip); the rest are g_w
+// tiles (64 x 128, K split over the NW waves).
+template <class T, int MTA, int KS, int NW, int SW>
 __global__ __launch_bounds__(NW * WAVE) void bwd_tail_kernel(const T* __restrict__ Qgy, const T* __restrict__ w,
                                                              const T* __restrict__ At, int ldA, int R, int L,
                                                              int Cy, int Cx, T* __restrict__ gx, int nstrip,
-                                                             int nz, int ngx, const T* __restrict__ Pgy,
+                                                             int ngx, const T* __restrict__ Pgy,
                                                              const T* __restrict__ xhat, T* __restrict__ gw,
                                                              int Kw, int gw_bx) {
   __shared__ float red[NW][8][4][WAVE];
-  __shared__ __attribute__((aligned(16))) GxShared<T, KS> gs;
+  __shared__ __attribute__((aligned(16))) GxShared<T, KS, SW> gs;
   const int id = blockIdx.x;
   if (id < ngx) {
-    const int rest = id / nstrip;
-    gx_fused_block<T, MTA, KS, NW>(Qgy, w, At, ldA, R, L, Cy, Cx, gx, id % nstrip, rest / nz, rest % nz, nz, red,
-                                   gs);
+    gx_fused_block<T, MTA, KS, NW, SW>(Qgy, w, At, ldA, R, L, Cy, Cx, gx, id % nstrip, id / nstrip,
+                                       reinterpret_cast<float (*)[SW][4][WAVE]>(&red[0][0][0][0]), gs);
   } else {
     // g_w = sum_b (P gy_b)^T x_hat_b: M = Cy, N = Cx, K = B*Rx (A stored [K][Cy])
     const int t = id - ngx;
@@ -559,21 +557,28 @@ hipError_t launch_expand(bool bf16_io, const void* At, int ldA, const void* Bz, 
                  : expand_t<float>(At, ldA, Bz, B, R, L, C, out, st);
 }
 
-template <class T, int MTA, int KS>
+template <class T, int MTA, int KS, int SW>
 static hipError_t bwd_tail_cfg(const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L, int Cy,
                                int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw,
                                hipStream_t st) {
   constexpr int NW = MTA == 1 ? 8 : 4;
-  const int nstrip = (Cx + 127) / 128;
-  // one token chunk per sample: each further chunk repeats the g_hat_x phase, whose read
-  // of the w strip costs more than the extra parallelism gains
-  const int nz = 1;
-  const int ngx = nstrip * B * nz;
+  const int nstrip = (Cx + 16 * SW - 1) / (16 * SW);
+  const int ngx = nstrip * B;
   const int gw_bx = (Cx + 127) / 128, gw_by = (Cy + 63) / 64;
-  hipLaunchKernelGGL((bwd_tail_kernel<T, MTA, KS, NW>), dim3(ngx + gw_bx * gw_by), dim3(NW * WAVE), 0, st,
-                     (const T*)Qgy, (const T*)w, (const T*)At, ldA, R, L, Cy, Cx, (T*)gx, nstrip, nz, ngx,
-                     (const T*)Pgy, (const T*)xhat, (T*)gw, Kw, gw_bx);
+  hipLaunchKernelGGL((bwd_tail_kernel<T, MTA, KS, NW, SW>), dim3(ngx + gw_bx * gw_by), dim3(NW * WAVE), 0, st,
+                     (const T*)Qgy, (const T*)w, (const T*)At, ldA, R, L, Cy, Cx, (T*)gx, nstrip, ngx, (const T*)Pgy,
+                     (const T*)xhat, (T*)gw, Kw, gw_bx);
   return hipGetLastError();
+}
+
+template <class T, int MTA, int KS>
+static hipError_t bwd_tail_sw(const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L, int Cy,
+                              int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw,
+                              hipStream_t st) {
+  // 64-column strips when 128-column ones would leave compute units without a g_x block
+  if ((long)((Cx + 127) / 128) * B < 256 && Cx > 64)
+    return bwd_tail_cfg<T, MTA, KS, 4>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, st);
+  return bwd_tail_cfg<T, MTA, KS, 8>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, st);
 }
 
 template <class T>
@@ -582,7 +587,7 @@ static hipError_t bwd_tail_t(const void* Qgy, const void* w, const void* At, int
   const int mta = (R + 15) / 16;
   const int ks = (R + MM<T>::KSTEP - 1) / MM<T>::KSTEP;
 #define BTC(MA, K) \
-  if (mta == MA && ks == K) return bwd_tail_cfg<T, MA, K>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, st);
+  if (mta == MA && ks == K) return bwd_tail_sw<T, MA, K>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, st);
   if constexpr (MM<T>::KSTEP == 32) {
     BTC(1, 1) BTC(2, 1) BTC(3, 2) BTC(4, 2)
   } else {
