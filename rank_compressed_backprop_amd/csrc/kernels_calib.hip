@@ -24,6 +24,7 @@ namespace instant {
 // second kernel adds them to the float64 sums in slice order.
 constexpr int ST = 128;           // statistics tile edge
 constexpr int SYRK_STAGES = 3;    // LDS ring depth (32 KB a stage; deeper rings measured no faster)
+constexpr int SYRK_LOADERS = 4;   // waves that only stream the ring, besides the four computing
 
 int syrk_tiles(int L) {
   const int T = (L + ST - 1) / ST;
@@ -74,12 +75,17 @@ __device__ inline void wait_oldest_stage(int younger) {
 constexpr int WPANEL = ST * 128;  // bytes per panel of a stage
 __device__ inline int wide_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <class T, int STAGES>
-__global__ __launch_bounds__(256) void syrk_kernel(const T* __restrict__ X, int B, int L, int C, int nsplit,
-                                                    const T* __restrict__ zpad, float* __restrict__ part) {
+// NLD = 0: the four compute waves also stream the ring; NLD = 4 or 8: that many more waves
+// only stream it (a wave sustains about a sixth of a compute unit's L2 read bandwidth).
+template <class T, int STAGES, int NLD>
+__global__ __launch_bounds__(64 * (4 + NLD)) void syrk_kernel(const T* __restrict__ X, int B, int L, int C,
+                                                              int nsplit, const T* __restrict__ zpad,
+                                                              float* __restrict__ part) {
   typedef MM<T> mm;
   typedef typename mm::frag frag;
-  static_assert(STAGES >= 2 && 8 * (STAGES - 2) <= 63, "outstanding loads must fit the vmcnt counter");
+  constexpr int LOADERS = NLD ? NLD : 4;
+  constexpr int HP = 16 / LOADERS;  // wave-loads per panel and loader
+  static_assert(STAGES >= 2 && 2 * HP * (STAGES - 2) <= 63, "outstanding loads must fit the vmcnt counter");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES][2][WPANEL];
   const int tid = threadIdx.x;
   const int lane = tid & (WAVE - 1);
@@ -107,8 +113,11 @@ __global__ __launch_bounds__(256) void syrk_kernel(const T* __restrict__ X, int 
   const int nq = end - beg;
 
   // A slice is a range of stages in (sample, channel) order; a stage past the last channel
-  // reads zeros. Wave-load j = 4 * wave + h moves rows 8j .. 8j+7 of a panel (1 KB).
+  // reads zeros. Wave-load j = HP * loader + h moves rows 8j .. 8j+7 of a panel (1 KB).
   constexpr int EPC = 16 / (int)sizeof(T);
+  const bool loader = NLD ? wave >= 4 : true;
+  const bool computer = wave < 4;
+  const int li = NLD ? wave - 4 : wave;
   auto issue = [&](int q, int stage) {
     const int b = q / pairs_c;
     const int k0 = (q - b * pairs_c) * 2 * mm::KSTEP;
@@ -118,8 +127,8 @@ __global__ __launch_bounds__(256) void syrk_kernel(const T* __restrict__ X, int 
       if (p == 1 && diag) break;
       const int tb = p == 0 ? ti : tj;
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const int j = 4 * wave + h;
+      for (int h = 0; h < HP; ++h) {
+        const int j = HP * li + h;
         const int rloc = 8 * j + (lane >> 3);
         const int chunk = (lane & 7) ^ wide_swz(rloc);
         const int row = tb * ST + rloc;
@@ -137,16 +146,20 @@ __global__ __launch_bounds__(256) void syrk_kernel(const T* __restrict__ X, int 
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc[t][u] = zero4();
 
+  if (loader) {
 #pragma unroll
-  for (int st = 0; st < STAGES - 1; ++st)
-    if (st < nq) issue(beg + st, st);
+    for (int st = 0; st < STAGES - 1; ++st)
+      if (st < nq) issue(beg + st, st);
+  }
   const int g = lane >> 4;
   for (int i = 0; i < nq; ++i) {
+    // (waves that issue no loads pass the count at once; all wait for their LDS reads)
     const int younger = (nq - 1 - i) < (STAGES - 2) ? (nq - 1 - i) : (STAGES - 2);
-    if (diag) wait_oldest_stage<4, STAGES - 2>(younger);
-    else wait_oldest_stage<8, STAGES - 2>(younger);
+    if (diag) wait_oldest_stage<HP, STAGES - 2>(younger);
+    else wait_oldest_stage<2 * HP, STAGES - 2>(younger);
     bare_barrier();
-    if (i + STAGES - 1 < nq) issue(beg + i + STAGES - 1, (i + STAGES - 1) % STAGES);
+    if (loader && i + STAGES - 1 < nq) issue(beg + i + STAGES - 1, (i + STAGES - 1) % STAGES);
+    if (!computer) continue;
     const unsigned char* pa = lds[i % STAGES][0];
     const unsigned char* pb = diag ? pa : lds[i % STAGES][1];
 #pragma unroll
@@ -166,6 +179,7 @@ __global__ __launch_bounds__(256) void syrk_kernel(const T* __restrict__ X, int 
     }
   }
 
+  if (!computer) return;
   // the partial tile in fragment order: one 16-byte store per lane and 16x16 tile
   float* __restrict__ out = part + ((size_t)s * ntiles + tile) * (ST * ST);
 #pragma unroll
@@ -208,8 +222,8 @@ template <class T>
 static hipError_t syrk_t(const void* X, int B, int L, int C, int nsplit, const void* zpad, float* part,
                          hipStream_t st) {
   dim3 grid(syrk_tiles(L) * nsplit);
-  hipLaunchKernelGGL((syrk_kernel<T, SYRK_STAGES>), grid, dim3(256), 0, st, (const T*)X, B, L, C, nsplit,
-                     (const T*)zpad, part);
+  hipLaunchKernelGGL((syrk_kernel<T, SYRK_STAGES, SYRK_LOADERS>), grid, dim3(64 * (4 + SYRK_LOADERS)), 0, st,
+                     (const T*)X, B, L, C, nsplit, (const T*)zpad, part);
   return hipGetLastError();
 }
 
