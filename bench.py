@@ -144,7 +144,10 @@ def main():
     _, info = lay.query()
     Rx, Ry = info.Rx, info.Ry
 
-    # ---- per-part timing with HIP events on the launch stream (outside the timed region)
+    # ---- per-part timing with HIP events on the launch stream, right after the timed loop.
+    # A pair of events around one launch inside the loop would add the markers' dispatch
+    # latency (about 3.5 us) to a 7.5 us kernel, so each part is timed over a run of
+    # consecutive launches on the same stream and resident batches.
     st = torch.cuda.current_stream()
 
     def ev_time(fn, reps):
@@ -219,6 +222,7 @@ def main():
         "roofline": {"kernel": "proj (forward compression x_hat = P x)", "bound": "hbm",
                      "achieved": gbs_fwd, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs_fwd / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "launch_us": t_fwd * 1e6, "launches_timed": reps,
                      "algorithmic_bytes_per_launch": bytes_fwd},
     }
 
