@@ -123,13 +123,25 @@ def main():
         s = lay.calibrate(xs[t], gys[t], B, finalize=(t == wl.n_cal - 1))
         assert s == rcb.INSTANT_OK, rcb.instant_status_str(s)
 
-    def step(i):
+    # the finalizing calls inside the timed loop, bracketed by HIP events on the launch
+    # stream (one pair per window; the span includes that step's statistics batch and the
+    # host round trip of the finalize)
+    fin_events = []
+
+    def step(i, timed=False):
         t = i % nb
         ph = i % wl.n_t
         lay.compress_fwd(xs[t], B, xhat)
         lay.backward(xhat, gys[t], w, B, gw, gx)
         if ph < wl.n_cal:
-            s = lay.calibrate(xs[t], gys[t], B, finalize=(ph == wl.n_cal - 1))
+            fin = ph == wl.n_cal - 1
+            if fin and timed:
+                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                ev[0].record()
+            s = lay.calibrate(xs[t], gys[t], B, finalize=fin)
+            if fin and timed:
+                ev[1].record()
+                fin_events.append(ev)
             if s != rcb.INSTANT_OK:
                 raise RuntimeError("calibration failed: " + rcb.instant_status_str(s))
 
@@ -138,9 +150,10 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.warmup, args.warmup + args.steps):
-        step(i)
+        step(i, timed=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    fin_loop = [a.elapsed_time(b) * 1e-3 for a, b in fin_events]
     _, info = lay.query()
     Rx, Ry = info.Rx, info.Ry
 
@@ -216,7 +229,9 @@ def main():
             "backward_pct_hbm_peak": 100.0 * bytes_bwd / t_bwd / 1e9 / HBM_PEAK_GBS,
             "backward_tokens_per_s": B * L / t_bwd, "backward_TFLOPs": flops_bwd / t_bwd / 1e12,
             "statistics_per_batch_us": t_acc * 1e6,
-            "finalize_ms": t_fin * 1e3, "host_enqueue_us_per_plain_step": t_issue * 1e6, "jacobi_sweeps": [info2.sweeps_x, info2.sweeps_g],
+            "finalize_ms": t_fin * 1e3,
+            "finalize_in_loop_ms": (sum(fin_loop) / len(fin_loop) * 1e3) if fin_loop else None,
+            "finalizes_in_loop": len(fin_loop), "host_enqueue_us_per_plain_step": t_issue * 1e6, "jacobi_sweeps": [info2.sweeps_x, info2.sweeps_g],
             "finalize_status": rcb.instant_status_str(s),
         },
         "roofline": {"kernel": "proj (forward compression x_hat = P x)", "bound": "hbm",

@@ -413,6 +413,19 @@ __device__ void jacobi_pair(const JacobiArgs& a, int side, int ba, int bb, int s
         wave_lds_sync();
       }
       if (__ballot(rotated) == 0) break;  // wave-uniform
+      // A second sweep starting with every pair under the rotation threshold would rotate
+      // nothing: skip it.
+      int left = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int idx = lane * 4 + e;
+        const int x = idx >> 4, y = idx & 15;
+        if (x < y) {
+          const double gx = sm.G[x][x], gy = sm.G[y][y], o = sm.G[x][y];
+          if (gx > floor_g && gy > floor_g && o * o > rt2 * gx * gy) left = 1;
+        }
+      }
+      if (__ballot(left) == 0) break;
     }
   }
   __syncthreads();
