@@ -278,10 +278,15 @@ __device__ inline void wave_lds_sync() { __asm__ volatile("s_waitcnt lgkmcnt(0)"
 __device__ inline void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 // Wait until *p >= v. Gives up (raising the abort flag) after SPIN_LIMIT polls or as soon
-// as another block raised it.
+// as another block raised it. The polls are relaxed and one acquire fence follows the
+// successful one: an acquire per poll would invalidate the XCD's L2 on every iteration,
+// under the feet of the blocks still staging their columns.
 __device__ bool wait_geq(const int* p, int v, int* abort) {
   for (long it = 0;; ++it) {
-    if (__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= v) return true;
+    if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= v) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      return true;
+    }
     if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return false;
     if (it > SPIN_LIMIT) {
       __hip_atomic_store(abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -493,14 +498,16 @@ __global__ __launch_bounds__(256) void jacobi_kernel(JacobiArgs a) {
       for (int round = 0; round < nbs - 1; ++round, ++rg) {
         const int ba = tourney(pair, round, nbs);
         const int bb = tourney(nbs - 1 - pair, round, nbs);
+        // thread 0 waits and acquires; the barrier orders the other waves' reads after it
         if (threadIdx.x == 0) sm.ok = wait_geq(&ver[ba], rg, a.abort) && wait_geq(&ver[bb], rg, a.abort);
         __syncthreads();
         if (!sm.ok) {
           aborted = true;
           break;
         }
-        acquire_agent();
         jacobi_pair(a, side, ba, bb, slot, sm, Ydyn);
+        // every wave's column stores have completed before thread 0 releases them
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (threadIdx.x == 0) {
           __threadfence();
