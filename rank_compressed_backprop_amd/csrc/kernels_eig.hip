@@ -327,6 +327,15 @@ __device__ void jacobi_pair(const JacobiArgs& a, int side, int ba, int bb, int s
   }
   __syncthreads();
 
+  // The accumulated rotation's entries of this thread's first update row, requested now so
+  // that their latency hides behind the Gram and the inner solve.
+  const int r0 = threadIdx.x;
+  double vpre[16];
+  if (r0 < a.ldw) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) vpre[q] = Vg[(size_t)sm.col[q] * a.ldw + r0];
+  }
+
   // G = Y^T Y: lane i reads four consecutive rows of column (i % 16), the four waves take
   // alternate 16-row steps, LDS sums the four partial tiles
   {
@@ -437,13 +446,13 @@ __device__ void jacobi_pair(const JacobiArgs& a, int side, int ba, int bb, int s
   if (!sm.need) return;
 
   // Y <- Y V (W from LDS, float64 arithmetic) and V_acc <- V_acc V (float64 in memory)
-  for (int r = threadIdx.x; r < a.ldw; r += 256) {
+  for (int r = r0; r < a.ldw; r += 256) {
     float y[16];
     double vv[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       y[q] = Y[q * a.ldw + r];
-      vv[q] = Vg[(size_t)sm.col[q] * a.ldw + r];
+      vv[q] = (r == r0) ? vpre[q] : Vg[(size_t)sm.col[q] * a.ldw + r];
     }
     double acc[16], accv[16];
 #pragma unroll
@@ -458,10 +467,13 @@ __device__ void jacobi_pair(const JacobiArgs& a, int side, int ba, int bb, int s
         accv[q] = fma(vp, vpq, accv[q]);
       }
     }
+    // device-scope stores write through the L2, so the release that publishes them has
+    // little dirty data to write back
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      W[(size_t)sm.col[q] * a.ldw + r] = (float)acc[q];
-      Vg[(size_t)sm.col[q] * a.ldw + r] = accv[q];
+      __hip_atomic_store(W + (size_t)sm.col[q] * a.ldw + r, (float)acc[q], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(Vg + (size_t)sm.col[q] * a.ldw + r, accv[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -510,9 +522,11 @@ __global__ __launch_bounds__(256) void jacobi_kernel(JacobiArgs a) {
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (threadIdx.x == 0) {
-          __threadfence();
-          __hip_atomic_store(&ver[ba], rg + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(&ver[bb], rg + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+          // one release for both counters (each release-ordered store would write the
+          // L2 back again)
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+          __hip_atomic_store(&ver[ba], rg + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(&ver[bb], rg + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
     }
