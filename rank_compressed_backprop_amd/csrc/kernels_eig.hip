@@ -66,7 +66,9 @@ constexpr int F_SCALE = 12;     // 2 doubles: ||C||_F^2 per side
 constexpr int F_BARRIER = 16;   // sweep barrier arrivals
 constexpr int F_ABORT = 17;     // a bounded wait timed out
 constexpr int F_NALIVE = 18;    // [2] columns above the noise floor
+constexpr int F_BARRIER2 = 20;  // Gram check arrivals
 constexpr int F_INFO = 24;      // [2][INFO_WORDS] copy of each side's info block
+constexpr int F_GMAX = 40;      // [3 slots][2 sides] Gram check maxima (float bits)
 constexpr size_t EIG_FLAGS_BYTES = 256;
 
 struct EigBufs {
@@ -255,6 +257,8 @@ struct JacobiArgs {
   unsigned* offmax;     // [3][2]
   int* out;             // [0..1] sweeps, [2..3] converged
   int* barrier;
+  int* barrier2;        // the Gram check's barrier
+  unsigned* gmax;       // [3][2] Gram check maxima (float bits)
   int* abort;
   int* version;         // [2][nb]
   const int* cols[2];   // column order per side (alive columns first)
@@ -268,6 +272,7 @@ struct JacobiSmem {
   float part[4][16][17];
   double G[16][17];
   double V[16][17];
+  float npart[2][16][16];  // Gram check: column norm partials [A/B][wave * 4 + group][column]
   int need;
   int ok;
 };
@@ -478,6 +483,72 @@ __device__ void jacobi_pair(const JacobiArgs& a, int side, int ba, int bb, int s
   }
 }
 
+// Convergence check of one side after a sweep: the largest relative off-diagonal
+// |G_pq| / sqrt(G_pp G_qq) of the Gram of its alive columns (pairs above the noise floor),
+// tile (ti, tj) of 16 columns each (ti <= tj), folded into *gmax. A sweep that left every
+// pair at or under the tolerance has converged the side; without this check only the next
+// sweep, which would rotate nothing, could tell.
+__device__ void gram_check_tile(const JacobiArgs& a, int side, int ti, int tj, JacobiSmem& sm, unsigned* gmax) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wave = threadIdx.x / WAVE;
+  const float* __restrict__ W = a.W[side];
+  const int na = a.n_alive[side];
+  const int ca = 16 * ti + (lane & 15), cb = 16 * tj + (lane & 15);
+  const bool oka = ca < na, okb = cb < na;
+  const float* __restrict__ pa = W + (size_t)(oka ? a.cols[side][ca] : 0) * a.ldw;
+  const float* __restrict__ pb = W + (size_t)(okb ? a.cols[side][cb] : 0) * a.ldw;
+  f32x4 acc = zero4();
+  float sa = 0.0f, sb = 0.0f;
+  for (int r0 = 16 * wave + 4 * (lane >> 4); r0 < a.ldw; r0 += 64) {
+    const f32x4 va = oka ? *reinterpret_cast<const f32x4*>(pa + r0) : zero4();
+    const f32x4 vb = okb ? *reinterpret_cast<const f32x4*>(pb + r0) : zero4();
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(va[g], vb[g], acc, 0, 0, 0);
+      sa += va[g] * va[g];
+      sb += vb[g] * vb[g];
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) sm.part[wave][4 * (lane >> 4) + v][lane & 15] = acc[v];
+  sm.npart[0][wave * 4 + (lane >> 4)][lane & 15] = sa;
+  sm.npart[1][wave * 4 + (lane >> 4)][lane & 15] = sb;
+  __syncthreads();
+  if (wave == 0) {
+    const double floor_g = NOISE_REL * a.scale[side];
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = lane * 4 + e;
+      const int x = idx >> 4, y = idx & 15;
+      if ((ti != tj || x < y) && 16 * ti + x < na && 16 * tj + y < na) {
+        const double g = (double)sm.part[0][x][y] + (double)sm.part[1][x][y] + (double)sm.part[2][x][y] +
+                         (double)sm.part[3][x][y];
+        double nx = 0.0, ny = 0.0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          nx += (double)sm.npart[0][k][x];
+          ny += (double)sm.npart[1][k][y];
+        }
+        if (nx > floor_g && ny > floor_g) m = fmaxf(m, (float)(fabs(g) / sqrt(nx * ny)));
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (lane == 0 && m > 0.0f) atomicMax(gmax, __float_as_uint(m));
+  }
+  __syncthreads();
+}
+
+// Tile idx of the upper triangle of a T x T grid of tiles, row by row.
+__device__ inline void upper_tile_ij(int idx, int T, int& ti, int& tj) {
+  ti = 0;
+  while (idx >= T - ti) {
+    idx -= T - ti;
+    ++ti;
+  }
+  tj = ti + idx;
+}
+
 // Block b handles pair (b mod nb/2) of side (b div nb/2) in every round. Round r of the
 // whole run (all sweeps counted) may start on column blocks a, b once their version
 // counters reached r; the pair then raises both to r + 1. Once per sweep all blocks meet
@@ -500,10 +571,13 @@ __global__ __launch_bounds__(256) void jacobi_kernel(JacobiArgs a) {
   int sweeps[2] = {0, 0};
   bool aborted = false;
   int rg = 0;  // this side's round index over the whole run
+  int checks = 0;
   for (int sweep = 0; sweep < a.max_sweeps && (active[0] || active[1]); ++sweep) {
     const int slot = sweep % 3;
     if (blockIdx.x == 0 && threadIdx.x < 2) {
       __hip_atomic_store(a.offmax + ((sweep + 1) % 3) * 2 + threadIdx.x, 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.gmax + ((sweep + 1) % 3) * 2 + threadIdx.x, 0u, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     }
     if (active[side] && mine) {
@@ -550,6 +624,41 @@ __global__ __launch_bounds__(256) void jacobi_kernel(JacobiArgs a) {
         sweeps[s] += 1;
         const unsigned bits = __hip_atomic_load(a.offmax + slot * 2 + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (__uint_as_float(bits) <= a.tol) active[s] = 0;
+      }
+    }
+    // Gram check of the sides still active; every block takes a share of the tiles
+    if (active[0] || active[1]) {
+      int nt[2], ntiles[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        nt[s] = (a.n_alive[s] + 15) / 16;
+        ntiles[s] = active[s] ? nt[s] * (nt[s] + 1) / 2 : 0;
+      }
+      for (int t = blockIdx.x; t < ntiles[0] + ntiles[1]; t += gridDim.x) {
+        const int s = t < ntiles[0] ? 0 : 1;
+        int ti, tj;
+        upper_tile_ij(t - (s ? ntiles[0] : 0), nt[s], ti, tj);
+        gram_check_tile(a, s, ti, tj, sm, a.gmax + slot * 2 + s);
+      }
+      checks += 1;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        __threadfence();
+        __hip_atomic_fetch_add(a.barrier2, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        sm.ok = wait_geq(a.barrier2, (int)gridDim.x * checks, a.abort);
+      }
+      __syncthreads();
+      if (!sm.ok) {
+        aborted = true;
+        break;
+      }
+      acquire_agent();
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (active[s]) {
+          const unsigned bits = __hip_atomic_load(a.gmax + slot * 2 + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (__uint_as_float(bits) <= a.tol) active[s] = 0;
+        }
       }
     }
     __syncthreads();  // sm.ok is rewritten in the next sweep
@@ -782,6 +891,8 @@ hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv
   ja.offmax = (unsigned*)(flags + F_OFFMAX);
   ja.out = flags + F_SWEEPS;
   ja.barrier = flags + F_BARRIER;
+  ja.barrier2 = flags + F_BARRIER2;
+  ja.gmax = (unsigned*)(flags + F_GMAX);
   ja.abort = flags + F_ABORT;
   ja.version = b.version;
   ja.cols[0] = b.cols[0];
