@@ -28,6 +28,8 @@
 namespace instant {
 
 constexpr int JB = 8;               // columns per Jacobi block
+constexpr int JT = 256;             // threads of a Jacobi workgroup (512 measured no faster)
+constexpr int JW = JT / 64;         // its waves
 constexpr int JAC_MAX_LDW = 2048;   // the 16 columns of a pair are staged in LDS (128 KB)
 // Columns whose squared norm is below NOISE_REL * ||C||_F^2 lie under float32 resolution
 // (sigma below 1e-5 of the total): their pairings are neither rotated nor counted.
@@ -269,10 +271,10 @@ struct JacobiArgs {
 
 struct JacobiSmem {
   int col[16];
-  float part[4][16][17];
+  float part[JW][16][17];
   double G[16][17];
   double V[16][17];
-  float npart[2][16][16];  // Gram check: column norm partials [A/B][wave * 4 + group][column]
+  float npart[2][4 * JW][16];  // Gram check: column norm partials [A/B][wave * 4 + group][column]
   int need;
   int ok;
 };
@@ -316,16 +318,16 @@ __device__ void jacobi_pair(const JacobiArgs& a, int side, int ba, int bb, int s
   // stage the columns, every load issued before any is used
   {
     const int n4 = a.ldw / 4;
-    for (int i0 = threadIdx.x; i0 < 16 * n4; i0 += 256 * 8) {
+    for (int i0 = threadIdx.x; i0 < 16 * n4; i0 += JT * 8) {
       f32x4 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * 256;
+        const int i = i0 + u * JT;
         if (i < 16 * n4) v[u] = *reinterpret_cast<const f32x4*>(W + (size_t)sm.col[i / n4] * a.ldw + 4 * (i % n4));
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * 256;
+        const int i = i0 + u * JT;
         if (i < 16 * n4) *reinterpret_cast<f32x4*>(&Y[(i / n4) * a.ldw + 4 * (i % n4)]) = v[u];
       }
     }
@@ -341,12 +343,12 @@ __device__ void jacobi_pair(const JacobiArgs& a, int side, int ba, int bb, int s
     for (int q = 0; q < 16; ++q) vpre[q] = Vg[(size_t)sm.col[q] * a.ldw + r0];
   }
 
-  // G = Y^T Y: lane i reads four consecutive rows of column (i % 16), the four waves take
-  // alternate 16-row steps, LDS sums the four partial tiles
+  // G = Y^T Y: lane i reads four consecutive rows of column (i % 16), the waves take
+  // alternate 16-row steps, LDS sums their partial tiles
   {
     const float* __restrict__ cp = Y + (lane & 15) * a.ldw;
     f32x4 acc = zero4();
-    for (int r0 = 16 * wave + 4 * (lane >> 4); r0 < a.ldw; r0 += 64) {
+    for (int r0 = 16 * wave + 4 * (lane >> 4); r0 < a.ldw; r0 += 16 * JW) {
       const f32x4 v = *reinterpret_cast<const f32x4*>(cp + r0);
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v[0], v[0], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v[1], v[1], acc, 0, 0, 0);
@@ -364,8 +366,10 @@ __device__ void jacobi_pair(const JacobiArgs& a, int side, int ba, int bb, int s
     for (int e = 0; e < 4; ++e) {
       const int idx = lane * 4 + e;
       const int x = idx >> 4, y = idx & 15;
-      sm.G[x][y] = (double)sm.part[0][x][y] + (double)sm.part[1][x][y] + (double)sm.part[2][x][y] +
-                   (double)sm.part[3][x][y];
+      double g = 0.0;
+#pragma unroll
+      for (int w = 0; w < JW; ++w) g += (double)sm.part[w][x][y];
+      sm.G[x][y] = g;
       sm.V[x][y] = (x == y) ? 1.0 : 0.0;
     }
     wave_lds_sync();
@@ -451,7 +455,7 @@ __device__ void jacobi_pair(const JacobiArgs& a, int side, int ba, int bb, int s
   if (!sm.need) return;
 
   // Y <- Y V (W from LDS, float64 arithmetic) and V_acc <- V_acc V (float64 in memory)
-  for (int r = r0; r < a.ldw; r += 256) {
+  for (int r = r0; r < a.ldw; r += JT) {
     float y[16];
     double vv[16];
 #pragma unroll
@@ -499,7 +503,7 @@ __device__ void gram_check_tile(const JacobiArgs& a, int side, int ti, int tj, J
   const float* __restrict__ pb = W + (size_t)(okb ? a.cols[side][cb] : 0) * a.ldw;
   f32x4 acc = zero4();
   float sa = 0.0f, sb = 0.0f;
-  for (int r0 = 16 * wave + 4 * (lane >> 4); r0 < a.ldw; r0 += 64) {
+  for (int r0 = 16 * wave + 4 * (lane >> 4); r0 < a.ldw; r0 += 16 * JW) {
     const f32x4 va = oka ? *reinterpret_cast<const f32x4*>(pa + r0) : zero4();
     const f32x4 vb = okb ? *reinterpret_cast<const f32x4*>(pb + r0) : zero4();
 #pragma unroll
@@ -522,11 +526,12 @@ __device__ void gram_check_tile(const JacobiArgs& a, int side, int ti, int tj, J
       const int idx = lane * 4 + e;
       const int x = idx >> 4, y = idx & 15;
       if ((ti != tj || x < y) && 16 * ti + x < na && 16 * tj + y < na) {
-        const double g = (double)sm.part[0][x][y] + (double)sm.part[1][x][y] + (double)sm.part[2][x][y] +
-                         (double)sm.part[3][x][y];
+        double g = 0.0;
+#pragma unroll
+        for (int w = 0; w < JW; ++w) g += (double)sm.part[w][x][y];
         double nx = 0.0, ny = 0.0;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < 4 * JW; ++k) {
           nx += (double)sm.npart[0][k][x];
           ny += (double)sm.npart[1][k][y];
         }
@@ -555,7 +560,7 @@ __device__ inline void upper_tile_ij(int idx, int T, int& ti, int& tj) {
 // at a counting barrier and read the same per-side maxima, so they take the same
 // decisions. The maxima rotate over three slots: slot (s+1) mod 3 is cleared during
 // sweep s, after every block has read it at the end of sweep s-2.
-__global__ __launch_bounds__(256) void jacobi_kernel(JacobiArgs a) {
+__global__ __launch_bounds__(JT) void jacobi_kernel(JacobiArgs a) {
   __shared__ JacobiSmem sm;
   extern __shared__ float Ydyn[];  // the pair's 16 columns, 16 * ldw floats
   const int nbmax = a.nb;
@@ -907,7 +912,7 @@ hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv
   ja.rot_tol = 0.25f * ja.tol;
   void* kargs[] = {&ja};
   const size_t dyn = (size_t)16 * e.ldw * sizeof(float);
-  err = hipLaunchCooperativeKernel((const void*)jacobi_kernel, dim3(e.nb), dim3(256), kargs, dyn, st);
+  err = hipLaunchCooperativeKernel((const void*)jacobi_kernel, dim3(e.nb), dim3(JT), kargs, dyn, st);
   if (err != hipSuccess) return err;
 
   hipLaunchKernelGGL(colnorm_kernel, dim3(L, 2), dim3(64), 0, st, sd, e.ldw, L);
