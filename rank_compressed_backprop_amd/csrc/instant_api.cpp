@@ -67,7 +67,7 @@ Layout layout_of(const instant_config* c) {
   l.SX = take(L * L * sizeof(double));
   l.SG = take(L * L * sizeof(double));
   l.zpad = take(256);
-  l.part = take((size_t)syrk_split_cap(c->L) * syrk_tiles(c->L) * SYRK_TILE * SYRK_TILE * sizeof(float));
+  l.part = take(2 * (size_t)syrk_split_cap(c->L) * syrk_tiles(c->L) * SYRK_TILE * SYRK_TILE * sizeof(float));
   l.eig = take(eig_workspace_bytes(c->L));
   l.sig_x = take(L * sizeof(float));
   l.sig_g = take(L * sizeof(float));
@@ -102,7 +102,10 @@ struct instant_layer {
 
   double* SX() const { return (double*)(ws + lay.SX); }
   double* SG() const { return (double*)(ws + lay.SG); }
-  float* part() const { return (float*)(ws + lay.part); }
+  // partial tiles of the statistics' split reduction, one region per statistic
+  float* part(int side) const {
+    return (float*)(ws + lay.part) + (size_t)side * syrk_split_cap(cfg.L) * syrk_tiles(cfg.L) * SYRK_TILE * SYRK_TILE;
+  }
   int* info_dev() const { return (int*)(ws + lay.info); }
   int* rank_dev() const { return (int*)(ws + lay.rank); }
   float* P32(int b) const { return (float*)(ws + lay.P32[b]); }
@@ -116,7 +119,7 @@ namespace {
 inline hipStream_t S(void* stream) { return (hipStream_t)stream; }
 inline instant_status hip_ok(hipError_t e) { return e == hipSuccess ? INSTANT_OK : INSTANT_E_HIP; }
 
-instant_status accumulate(instant_layer* h, const void* t, int B, int C, double* Sacc, hipStream_t st) {
+int syrk_nsplit(const instant_layer* h, int B, int C) {
   const int kstep = h->bf16 ? 32 : 16;
   const int stages = ((C + kstep - 1) / kstep + 1) / 2;  // two k-steps per ring stage
   const long total = (long)B * stages;
@@ -124,9 +127,16 @@ instant_status accumulate(instant_layer* h, const void* t, int B, int C, double*
   // to give every compute unit a tile-slice, a multiple of 8 when there are 16 or more
   int nsplit = (int)std::min<long>(syrk_split_cap(h->cfg.L), std::max<long>(1, total / 16));
   if (nsplit >= 16) nsplit -= nsplit % 8;
-  hipError_t e = launch_syrk(h->bf16, t, B, h->cfg.L, C, nsplit, h->ws + h->lay.zpad, h->part(), st);
-  if (e != hipSuccess) return INSTANT_E_HIP;
-  return hip_ok(launch_syrk_reduce(h->part(), nsplit, h->cfg.L, Sacc, st));
+  return nsplit;
+}
+
+// Both statistics of a batch (either input may be NULL) in one SYRK launch.
+instant_status accumulate(instant_layer* h, const void* x, const void* gy, int B, hipStream_t st) {
+  SyrkSide sides[2];
+  int n = 0;
+  if (x) sides[n++] = SyrkSide{x, h->cfg.Cx, syrk_nsplit(h, B, h->cfg.Cx), h->part(0), h->SX()};
+  if (gy) sides[n++] = SyrkSide{gy, h->cfg.Cy, syrk_nsplit(h, B, h->cfg.Cy), h->part(1), h->SG()};
+  return hip_ok(launch_syrk(h->bf16, sides, n, B, h->cfg.L, h->ws + h->lay.zpad, st));
 }
 
 }  // namespace
@@ -181,14 +191,11 @@ INSTANT_API instant_status instant_calibrate(instant_layer* h, const void* x, co
     const int64_t nx = h->nx + (x ? B : 0), ng = h->ng + (gy ? B : 0);
     if (nx == 0 || ng == 0) return INSTANT_E_STATE;
   }
-  instant_status s;
-  if (x) {
-    if ((s = accumulate(h, x, B, h->cfg.Cx, h->SX(), st)) != INSTANT_OK) return s;
-    h->nx += B;
-  }
-  if (gy) {
-    if ((s = accumulate(h, gy, B, h->cfg.Cy, h->SG(), st)) != INSTANT_OK) return s;
-    h->ng += B;
+  if (x || gy) {
+    const instant_status s = accumulate(h, x, gy, B, st);
+    if (s != INSTANT_OK) return s;
+    if (x) h->nx += B;
+    if (gy) h->ng += B;
   }
   if (!finalize) return INSTANT_OK;
 

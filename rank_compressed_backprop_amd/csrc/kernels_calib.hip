@@ -78,9 +78,8 @@ __device__ inline int wide_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 // NLD = 0: the four compute waves also stream the ring; NLD = 4 or 8: that many more waves
 // only stream it (a wave sustains about a sixth of a compute unit's L2 read bandwidth).
 template <class T, int STAGES, int NLD>
-__global__ __launch_bounds__(64 * (4 + NLD)) void syrk_kernel(const T* __restrict__ X, int B, int L, int C,
-                                                              int nsplit, const T* __restrict__ zpad,
-                                                              float* __restrict__ part) {
+__global__ __launch_bounds__(64 * (4 + NLD)) void syrk_kernel(SyrkSide s0, SyrkSide s1, int B, int L,
+                                                              const T* __restrict__ zpad) {
   typedef MM<T> mm;
   typedef typename mm::frag frag;
   constexpr int LOADERS = NLD ? NLD : 4;
@@ -92,8 +91,15 @@ __global__ __launch_bounds__(64 * (4 + NLD)) void syrk_kernel(const T* __restric
   const int wave = tid / WAVE;
   const int Tn = (L + ST - 1) / ST;
   const int ntiles = Tn * (Tn + 1) / 2;
+  // blocks [0, ntiles * s0.nsplit) serve the first statistic, the rest the second
+  int lin = blockIdx.x;
+  const bool second = lin >= ntiles * s0.nsplit;
+  if (second) lin -= ntiles * s0.nsplit;
+  const T* __restrict__ X = (const T*)(second ? s1.X : s0.X);
+  const int C = second ? s1.C : s0.C;
+  const int nsplit = second ? s1.nsplit : s0.nsplit;
+  float* __restrict__ part = second ? s1.part : s0.part;
   int tile, s;
-  const int lin = blockIdx.x;
   if (nsplit % 8 == 0) {
     const int xcd = lin % 8, kq = lin / 8;
     s = xcd + 8 * (kq / ntiles);
@@ -190,8 +196,11 @@ __global__ __launch_bounds__(64 * (4 + NLD)) void syrk_kernel(const T* __restric
 }
 
 // S[i][j] += sum_s part[s][tile] in split order, float64, for the upper-triangle tiles.
-__global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restrict__ part, int nsplit, int ntiles,
-                                                          int L, double* __restrict__ S) {
+__global__ __launch_bounds__(256) void syrk_reduce_kernel(SyrkSide s0, SyrkSide s1, int ntiles, int L) {
+  const SyrkSide& sd = blockIdx.z ? s1 : s0;
+  const float* __restrict__ part = sd.part;
+  const int nsplit = sd.nsplit;
+  double* __restrict__ S = sd.S;
   const int tile = blockIdx.x;
   const int e = blockIdx.y * 256 + threadIdx.x;  // fragment-order index, see syrk_kernel
   const int Tn = (L + ST - 1) / ST;
@@ -219,24 +228,23 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(const float* __restric
 }
 
 template <class T>
-static hipError_t syrk_t(const void* X, int B, int L, int C, int nsplit, const void* zpad, float* part,
-                         hipStream_t st) {
-  dim3 grid(syrk_tiles(L) * nsplit);
-  hipLaunchKernelGGL((syrk_kernel<T, SYRK_STAGES, SYRK_LOADERS>), grid, dim3(64 * (4 + SYRK_LOADERS)), 0, st,
-                     (const T*)X, B, L, C, nsplit, (const T*)zpad, part);
+static hipError_t syrk_t(const SyrkSide* sides, int nsides, int B, int L, const void* zpad, hipStream_t st) {
+  const SyrkSide s0 = sides[0];
+  const SyrkSide s1 = nsides > 1 ? sides[1] : SyrkSide{nullptr, 0, 0, nullptr, nullptr};
+  const int nt = syrk_tiles(L);
+  hipLaunchKernelGGL((syrk_kernel<T, SYRK_STAGES, SYRK_LOADERS>), dim3(nt * (s0.nsplit + s1.nsplit)),
+                     dim3(64 * (4 + SYRK_LOADERS)), 0, st, s0, s1, B, L, (const T*)zpad);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid(nt, ST * ST / 256, nsides);  // 64 blocks of 256 elements per tile and statistic
+  hipLaunchKernelGGL(syrk_reduce_kernel, grid, dim3(256), 0, st, s0, s1, nt, L);
   return hipGetLastError();
 }
 
-hipError_t launch_syrk(bool bf16_io, const void* X, int B, int L, int C, int nsplit, const void* zpad, float* part,
+hipError_t launch_syrk(bool bf16_io, const SyrkSide* sides, int nsides, int B, int L, const void* zpad,
                        hipStream_t st) {
-  return bf16_io ? syrk_t<bf16>(X, B, L, C, nsplit, zpad, part, st)
-                 : syrk_t<float>(X, B, L, C, nsplit, zpad, part, st);
-}
-
-hipError_t launch_syrk_reduce(const float* part, int nsplit, int L, double* S, hipStream_t st) {
-  dim3 grid(syrk_tiles(L), ST * ST / 256);  // 64 blocks of 256 elements per tile
-  hipLaunchKernelGGL(syrk_reduce_kernel, grid, dim3(256), 0, st, part, nsplit, syrk_tiles(L), L, S);
-  return hipGetLastError();
+  if (nsides < 1 || nsides > 2) return hipErrorInvalidValue;
+  return bf16_io ? syrk_t<bf16>(sides, nsides, B, L, zpad, st) : syrk_t<float>(sides, nsides, B, L, zpad, st);
 }
 
 // I/O-dtype copies: PQ rows [0, Rx) = P, [Rx, Rx+Ry) = Q with ld ldL (zero beyond L), and

@@ -684,8 +684,9 @@ __global__ __launch_bounds__(JT) void jacobi_kernel(JacobiArgs a) {
 constexpr int MAX_L = 2048;
 constexpr int INFO_STATUS = 0, INFO_K = 1, INFO_R = 2, INFO_C = 3, INFO_KEPT = 4, INFO_KEPTK = 6;
 
-// One block of 1024 threads: sort the L column norms (descending, ties by column index),
-// energy prefix in float64, truncation, compensation and P = c * U_R^T.
+// One block of 1024 threads per side: sort the L column norms (descending, ties by column
+// index), energy prefix in float64 (a block scan), truncation, compensation and
+// P = c * U_R^T.
 struct TruncArgs {
   const float* W[2];
   const float* nrm[2];
@@ -707,8 +708,10 @@ __global__ __launch_bounds__(1024) void truncate_build_kernel(TruncArgs a, int l
   const int p = a.p, comp = a.comp, R_max = a.R_max;
   __shared__ float key[MAX_L];
   __shared__ int idx[MAX_L];
+  __shared__ double pre[MAX_L];
+  __shared__ double scan[1024];
   __shared__ double prefix_last, prefix_k, prefix_R;
-  __shared__ int sk, sR, sstatus;
+  __shared__ int sk, sR, sstatus, kfirst;
   __shared__ float sc;
   const int tid = threadIdx.x;
   int Lp2 = 1;
@@ -741,33 +744,44 @@ __global__ __launch_bounds__(1024) void truncate_build_kernel(TruncArgs a, int l
   }
   for (int i = tid; i < L; i += 1024) sigma_out[i] = key[i];
 
+  // float64 prefix of sigma^2 in sorted order: thread t owns entries 2t and 2t+1 and the
+  // block scans the pair sums (pre[i] = sum_{j <= i} sigma_j^2)
+  {
+    const double a0 = 2 * tid < L ? (double)key[2 * tid] * (double)key[2 * tid] : 0.0;
+    const double a1 = 2 * tid + 1 < L ? (double)key[2 * tid + 1] * (double)key[2 * tid + 1] : 0.0;
+    scan[tid] = a0 + a1;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const double v = tid >= off ? scan[tid - off] : 0.0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const double before = scan[tid] - (a0 + a1);
+    if (2 * tid < L) pre[2 * tid] = before + a0;
+    if (2 * tid + 1 < L) pre[2 * tid + 1] = before + a0 + a1;
+    if (tid == 0) kfirst = L;
+    __syncthreads();
+    // k = the smallest j with pre[j - 1] >= eps * E
+    const double thr = (double)eps * pre[L - 1];
+    for (int i = tid; i < L; i += 1024)
+      if (pre[i] >= thr && (i == 0 || pre[i - 1] < thr)) atomicMin(&kfirst, i);
+    __syncthreads();
+  }
+
   if (tid == 0) {
     int status = 0;
     if (flags[F_BAD + side]) status = 6;        // non-finite statistics
     else if (!flags[F_CONV + side]) status = 7;  // no convergence
-    // ordered float64 prefix of sigma^2
-    double run = 0.0;
-    for (int i = 0; i < L; ++i) {
-      const double sgm = (double)key[i];
-      run += sgm * sgm;
-    }
-    const double E = run;
+    const double E = pre[L - 1];
     int k = 0;
     double Sk = 0.0, SR = 0.0;
     if (status == 0 && !(E > 0.0)) status = (E == 0.0) ? 5 : 6;
     if (status == 0) {
-      const double thr = (double)eps * E;
-      run = 0.0;
-      for (int i = 0; i < L; ++i) {
-        const double sgm = (double)key[i];
-        run += sgm * sgm;
-        if (run >= thr) {
-          k = i + 1;
-          Sk = run;
-          break;
-        }
-      }
-      if (k == 0) {  // rounding made the total fall short of eps*E: only possible at eps == 1
+      if (kfirst < L) {
+        k = kfirst + 1;
+        Sk = pre[kfirst];
+      } else {  // rounding made the total fall short of eps*E: only possible at eps == 1
         k = L;
         Sk = E;
       }
@@ -776,12 +790,7 @@ __global__ __launch_bounds__(1024) void truncate_build_kernel(TruncArgs a, int l
     if (status == 0 && R > R_max) status = 4;
     float c = 1.0f;
     if (status == 0) {
-      run = 0.0;
-      for (int i = 0; i < R; ++i) {
-        const double sgm = (double)key[i];
-        run += sgm * sgm;
-      }
-      SR = run;
+      SR = pre[R - 1];
       if (comp == 0) c = (float)(1.0 / sqrt(SR));
       else if (comp == 2) c = (float)sqrt(E / SR);
     }

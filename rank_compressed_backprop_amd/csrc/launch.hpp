@@ -33,13 +33,19 @@ hipError_t launch_bwd_tail(bool bf16_io, const void* Qgy, const void* w, const v
 
 // ---- calibration ([KD1], [KD2])
 
-// Upper-triangle tile partial sums of sum_b X_b X_b^T over `nsplit` slices of the
-// batch*channel reduction, written as float32 to part [nsplit][ntiles][128*128].
-// zpad: 16 zero bytes in device memory (read in place of out-of-range data).
-hipError_t launch_syrk(bool bf16_io, const void* X, int B, int L, int C, int nsplit, const void* zpad, float* part,
+// One statistic of a batch: S += sum_b X_b X_b^T for X [B][L][C] (float64 upper-triangle
+// tiles of S), through nsplit slices of the batch*channel reduction whose float32 partial
+// tiles go to part [nsplit][ntiles][128*128], summed into S in slice order.
+struct SyrkSide {
+  const void* X;
+  int C, nsplit;
+  float* part;
+  double* S;
+};
+// The statistics of one batch: one or two sides in one SYRK launch, then one reduction
+// launch. zpad: 256 zero bytes in device memory (read in place of out-of-range data).
+hipError_t launch_syrk(bool bf16_io, const SyrkSide* sides, int nsides, int B, int L, const void* zpad,
                        hipStream_t st);
-// S[i][j] += sum_s part[s] (fixed order) for the upper-triangle tiles.
-hipError_t launch_syrk_reduce(const float* part, int nsplit, int L, double* S, hipStream_t st);
 int syrk_tiles(int L);
 
 // Eigen-decomposition of both statistics (C = S * inv_n, float64 upper-triangle sums)
