@@ -146,7 +146,8 @@ instant_status instant_get_projections(instant_layer* h, float* P, float* Q, flo
                                        float* sigma_g, void* stream);
 
 /* Copy out the current statistic means C_X, C_G [L, L] float64 (device pointers,
- * either may be NULL), i.e. the running sums divided by the samples seen so far. */
+ * either may be NULL), i.e. the running sums divided by the samples seen so far.
+ * Errors: E_ARG, E_STATE (a requested side has no samples in the current window), E_HIP. */
 instant_status instant_get_statistics(instant_layer* h, double* C_X, double* C_G, void* stream);
 
 /* Name of a status code. */

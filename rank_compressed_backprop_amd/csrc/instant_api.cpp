@@ -134,8 +134,9 @@ int syrk_nsplit(const instant_layer* h, int B, int C) {
 instant_status accumulate(instant_layer* h, const void* x, const void* gy, int B, hipStream_t st) {
   SyrkSide sides[2];
   int n = 0;
-  if (x) sides[n++] = SyrkSide{x, h->cfg.Cx, syrk_nsplit(h, B, h->cfg.Cx), h->part(0), h->SX()};
-  if (gy) sides[n++] = SyrkSide{gy, h->cfg.Cy, syrk_nsplit(h, B, h->cfg.Cy), h->part(1), h->SG()};
+  // the first batch of a window overwrites the sums, so a finalize need not clear them
+  if (x) sides[n++] = SyrkSide{x, h->cfg.Cx, syrk_nsplit(h, B, h->cfg.Cx), h->part(0), h->SX(), h->nx == 0};
+  if (gy) sides[n++] = SyrkSide{gy, h->cfg.Cy, syrk_nsplit(h, B, h->cfg.Cy), h->part(1), h->SG(), h->ng == 0};
   return hip_ok(launch_syrk(h->bf16, sides, n, B, h->cfg.L, h->ws + h->lay.zpad, st));
 }
 
@@ -211,10 +212,10 @@ INSTANT_API instant_status instant_calibrate(instant_layer* h, const void* x, co
   out.sigma_g = (float*)(h->ws + h->lay.sig_g);
   out.info_x = h->info_dev();
   out.info_g = h->info_dev() + INFO_WORDS;
-  // Queued before the host reads the outcome, so the finalize costs one round trip:
-  // the I/O copies of the new projections go to the inactive buffer t (harmless if
-  // the finalize fails: t only becomes active on success), and the statistics window
-  // is consumed whatever the outcome.
+  // Queued before the host reads the outcome, so the finalize costs one round trip: the
+  // I/O copies of the new projections go to the inactive buffer t (harmless if the
+  // finalize fails: t only becomes active on success). The statistics window is consumed
+  // whatever the outcome: the next batch overwrites the sums.
   struct Tail {
     instant_layer* h;
     int t;
@@ -223,13 +224,9 @@ INSTANT_API instant_status instant_calibrate(instant_layer* h, const void* x, co
   out.before_readback = [](void* ctx, hipStream_t st) -> hipError_t {
     const Tail& tl = *(const Tail*)ctx;
     instant_layer* hh = tl.h;
-    hipError_t e = launch_build_io(hh->bf16, hh->P32(tl.t), hh->Q32(tl.t), hh->info_dev() + 2,
-                                   hh->info_dev() + INFO_WORDS + 2, hh->cfg.L, hh->lay.ldL, hh->cfg.R_max,
-                                   hh->PQ(tl.t), hh->Qt(tl.t), LD_QT, st);
-    // SG follows SX in the workspace: one fill clears both (and the padding between)
-    const size_t sbytes = (hh->lay.SG - hh->lay.SX) + (size_t)hh->cfg.L * hh->cfg.L * sizeof(double);
-    if (e == hipSuccess) e = launch_zero(hh->SX(), sbytes, st);
-    return e;
+    return launch_build_io(hh->bf16, hh->P32(tl.t), hh->Q32(tl.t), hh->info_dev() + 2,
+                           hh->info_dev() + INFO_WORDS + 2, hh->cfg.L, hh->lay.ldL, hh->cfg.R_max, hh->PQ(tl.t),
+                           hh->Qt(tl.t), LD_QT, st);
   };
   int flags[EIG_HOST_FLAGS];
   hipError_t e = run_eig(h->SX(), h->SG(), 1.0 / (double)h->nx, 1.0 / (double)h->ng, h->cfg.L, h->cfg.max_sweeps,

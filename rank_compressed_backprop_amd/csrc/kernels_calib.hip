@@ -195,7 +195,8 @@ __global__ __launch_bounds__(64 * (4 + NLD)) void syrk_kernel(SyrkSide s0, SyrkS
       *reinterpret_cast<f32x4*>(out + (((wave * 16 + t * 4 + u) * WAVE + lane) * 4)) = acc[t][u];
 }
 
-// S[i][j] += sum_s part[s][tile] in split order, float64, for the upper-triangle tiles.
+// S[i][j] += sum_s part[s][tile] in split order, float64, for the upper-triangle tiles (or
+// S[i][j] = that sum for a statistic's first batch).
 __global__ __launch_bounds__(256) void syrk_reduce_kernel(SyrkSide s0, SyrkSide s1, int ntiles, int L) {
   const SyrkSide& sd = blockIdx.z ? s1 : s0;
   const float* __restrict__ part = sd.part;
@@ -224,13 +225,14 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(SyrkSide s0, SyrkSide 
     acc += (double)v3;
   }
   for (; s < nsplit; ++s) acc += (double)pp[s * stride];
-  S[(size_t)i * L + j] += acc;
+  if (sd.overwrite) S[(size_t)i * L + j] = acc;
+  else S[(size_t)i * L + j] += acc;
 }
 
 template <class T>
 static hipError_t syrk_t(const SyrkSide* sides, int nsides, int B, int L, const void* zpad, hipStream_t st) {
   const SyrkSide s0 = sides[0];
-  const SyrkSide s1 = nsides > 1 ? sides[1] : SyrkSide{nullptr, 0, 0, nullptr, nullptr};
+  const SyrkSide s1 = nsides > 1 ? sides[1] : SyrkSide{nullptr, 0, 0, nullptr, nullptr, 0};
   const int nt = syrk_tiles(L);
   hipLaunchKernelGGL((syrk_kernel<T, SYRK_STAGES, SYRK_LOADERS>), dim3(nt * (s0.nsplit + s1.nsplit)),
                      dim3(64 * (4 + SYRK_LOADERS)), 0, st, s0, s1, B, L, (const T*)zpad);

@@ -138,10 +138,15 @@ struct EigSides {
 };
 
 // W[c][r] = S[min(r,c)][max(r,c)] * inv_n (column-major, zero padding); flags non-finite sums.
-__global__ __launch_bounds__(256) void jacobi_prep_kernel(EigSides a, int L, int ldw, int* __restrict__ bad) {
+// For a warm start it also rounds column c of the accumulated rotation to float32 (V32):
+// rounding V only perturbs W = C V at float32 resolution, the rotation itself stays float64.
+__global__ __launch_bounds__(256) void jacobi_prep_kernel(EigSides a, int L, int ldw, int warm,
+                                                          int* __restrict__ bad) {
   const int c = blockIdx.x, s = blockIdx.y;
   const double* S = a.S[s];
   float* W = a.Wp[s];
+  if (warm)
+    for (int r = threadIdx.x; r < ldw; r += 256) a.V32[s][(size_t)c * ldw + r] = (float)a.V[s][(size_t)c * ldw + r];
   for (int r = threadIdx.x; r < ldw; r += 256) {
     float v = 0.0f;
     if (r < L && c < L) {
@@ -160,15 +165,6 @@ __global__ __launch_bounds__(256) void identity_kernel(EigSides a, int ldw) {
   const int c = blockIdx.x;
   double* V = a.V[blockIdx.y];
   for (int r = threadIdx.x; r < ldw; r += 256) V[(size_t)c * ldw + r] = (r == c) ? 1.0 : 0.0;
-}
-
-// Warm start, step 1: the accumulated rotation rounded to float32 (column-major, as stored).
-// Rounding V here only perturbs W = C V at float32 resolution; the rotation itself stays
-// float64.
-__global__ __launch_bounds__(256) void v_to_f32_kernel(EigSides a, size_t n) {
-  const double* V = a.V[blockIdx.y];
-  float* V32 = a.V32[blockIdx.y];
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) V32[i] = (float)V[i];
 }
 
 // Column norms of W: sigma_c = ||W[:, c]||, c < L.
@@ -259,6 +255,7 @@ struct JacobiArgs {
   const double* scale;  // [2] ||C||_F^2, invariant under the rotations
   unsigned* offmax;     // [3][2]
   int* out;             // [0..1] sweeps, [2..3] converged
+  float* nrm[2];        // final column norms (written at the end)
   int* barrier;
   int* barrier2;        // the Gram check's barrier
   unsigned* gmax;       // [3][2] Gram check maxima (float bits)
@@ -669,6 +666,19 @@ __global__ __launch_bounds__(JT) void jacobi_kernel(JacobiArgs a) {
     }
     __syncthreads();  // sm.ok is rewritten in the next sweep
   }
+  // Final column norms of both sides (sigma = ||W[:, c]||, c < L): every block passed the
+  // last sweep barrier, so W is complete; one wave per column.
+  if (!aborted) {
+    const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+    for (int q = blockIdx.x * JW + wave; q < 2 * a.L; q += gridDim.x * JW) {
+      const int s = q / a.L, c = q - s * a.L;
+      const float* __restrict__ col = a.W[s] + (size_t)c * a.ldw;
+      float acc = 0.0f;
+      for (int r = lane; r < a.L; r += WAVE) acc += col[r] * col[r];
+      for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+      if (lane == 0) a.nrm[s][c] = sqrtf(acc);
+    }
+  }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     a.out[0] = sweeps[0];
     a.out[1] = sweeps[1];
@@ -879,13 +889,11 @@ hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv
     sd.nrm[s] = b.nrm[s];
     sd.cols[s] = b.cols[s];
   }
-  hipLaunchKernelGGL(jacobi_prep_kernel, dim3(e.ncols, 2), dim3(256), 0, st, sd, L, e.ldw, flags + F_BAD);
+  hipLaunchKernelGGL(jacobi_prep_kernel, dim3(e.ncols, 2), dim3(256), 0, st, sd, L, e.ldw, warm ? 1 : 0,
+                     flags + F_BAD);
   if (warm) {
     // W[c][r] = sum_k V[k][c] C[k][r]: A = V^T stored [ncols][ldw] (k contiguous), B = C
     // stored [k][r] (r contiguous), both float32, on the matrix cores; one batch per side
-    const size_t nv = (size_t)e.ncols * e.ldw;
-    hipLaunchKernelGGL(v_to_f32_kernel, dim3((unsigned)std::min<size_t>((nv + 255) / 256, 1024), 2), dim3(256), 0, st,
-                       sd, nv);
     if ((err = launch_gemm(false, false, b.V32[0], e.ldw, (size_t)(b.V32[1] - b.V32[0]), b.Wtmp[0], e.ldw,
                            (size_t)(b.Wtmp[1] - b.Wtmp[0]), b.W[0], e.ldw, (size_t)(b.W[1] - b.W[0]), 2, e.ncols,
                            e.ldw, L, st)) != hipSuccess)
@@ -905,6 +913,8 @@ hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv
   ja.scale = scale;
   ja.offmax = (unsigned*)(flags + F_OFFMAX);
   ja.out = flags + F_SWEEPS;
+  ja.nrm[0] = b.nrm[0];
+  ja.nrm[1] = b.nrm[1];
   ja.barrier = flags + F_BARRIER;
   ja.barrier2 = flags + F_BARRIER2;
   ja.gmax = (unsigned*)(flags + F_GMAX);
@@ -925,7 +935,6 @@ hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv
   err = hipLaunchCooperativeKernel((const void*)jacobi_kernel, dim3(e.nb), dim3(JT), kargs, dyn, st);
   if (err != hipSuccess) return err;
 
-  hipLaunchKernelGGL(colnorm_kernel, dim3(L, 2), dim3(64), 0, st, sd, e.ldw, L);
   TruncArgs ta;
   for (int s = 0; s < 2; ++s) {
     ta.W[s] = b.W[s];

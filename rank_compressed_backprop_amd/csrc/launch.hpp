@@ -41,6 +41,7 @@ struct SyrkSide {
   int C, nsplit;
   float* part;
   double* S;
+  int overwrite;  // S = the batch's sum instead of S += it (the first batch of a window)
 };
 // The statistics of one batch: one or two sides in one SYRK launch, then one reduction
 // launch. zpad: 256 zero bytes in device memory (read in place of out-of-range data).
