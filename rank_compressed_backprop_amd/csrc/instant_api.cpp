@@ -97,6 +97,7 @@ struct instant_layer {
   bool warm;   // the eigensolver's accumulated rotation from the last finalize is usable
   int Rx, Ry;
   int64_t nx, ng;
+  int ncu;  // compute units of the device the handle was created on
   instant_info info;
   instant_status last;
 
@@ -163,6 +164,13 @@ INSTANT_API instant_status instant_create(instant_layer** h, const instant_confi
   L->nx = L->ng = 0;
   std::memset(&L->info, 0, sizeof(L->info));
   L->last = INSTANT_OK;
+  int dev = 0;
+  L->ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&L->ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || L->ncu < 1) {
+    delete L;
+    return INSTANT_E_HIP;
+  }
   // statistics start at zero; the rest of the workspace is written before it is read
   hipError_t e = launch_zero(L->SX(), (size_t)cfg->L * cfg->L * sizeof(double), S(stream));
   if (e == hipSuccess) e = launch_zero(L->ws + L->lay.zpad, 256, S(stream));
@@ -295,7 +303,7 @@ INSTANT_API instant_status instant_backward(instant_layer* h, const void* xhat, 
   if (gx_fused_applies(h->bf16, B, Cx, Cy)) {
     // g_x_b = Q^T ((Q gy_b) w) with w resident in L2, and g_w, in one launch
     if (e == hipSuccess)
-      e = launch_bwd_tail(h->bf16, Qgy, w, h->Qt(a), LD_QT, B, Ry, L, Cy, Cx, gx, Pgy, xhat, gw, B * Rx, st);
+      e = launch_bwd_tail(h->bf16, Qgy, w, h->Qt(a), LD_QT, B, Ry, L, Cy, Cx, gx, Pgy, xhat, gw, B * Rx, h->ncu, st);
   } else {
     // g_w = sum_b (P gy_b)^T x_hat_b: M = Cy, N = Cx, K = B * Rx
     if (e == hipSuccess) e = launch_gemm(h->bf16, true, Pgy, Cy, 0, xhat, Cx, 0, gw, Cx, 0, 1, Cy, Cx, B * Rx, st);

@@ -115,17 +115,18 @@ __global__ __launch_bounds__(NW * WAVE) void proj_kernel(const T* __restrict__ A
 // B is [K][ldb] (n contiguous); the wave covers 128 columns.
 // Grid: (ceil(N / 128), ceil(M / rows per wave), batch); the NW waves of a block split K,
 // each issuing the loads of U steps before any product.
-// Block (bx, by, bz) of the grid described above; `red` is NW * 8 KB of LDS.
+// Block (bx, by, bz) of the grid described above, computed by NW waves numbered `wave` =
+// 0 .. NW-1 (all waves of the workgroup call it the same number of times: it holds block
+// barriers); `red` is NW * 8 KB of LDS.
 template <class T, bool A_TRANS, int MT, int NW, int U>
 __device__ __forceinline__ void gemm_block(const T* __restrict__ A, int lda, size_t strideA,
                                            const T* __restrict__ Bm, int ldb, size_t strideB, T* __restrict__ Cm,
                                            int ldc, size_t strideC, int M, int N, int K, int bx, int by, int bz,
-                                           float (*red)[8][4][WAVE]) {
+                                           int wave, float (*red)[8][4][WAVE]) {
   typedef MM<T> mm;
   typedef typename mm::frag frag;
   const int lane = threadIdx.x & (WAVE - 1);
-  const int wave = threadIdx.x / WAVE;
-  const int z = bz;
+    const int z = bz;
   A += z * strideA;
   Bm += z * strideB;
   Cm += z * strideC;
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_kernel(const T* __restrict__ A
                                                          int M, int N, int K) {
   __shared__ float red[NW][8][4][WAVE];
   gemm_block<T, A_TRANS, MT, NW, U>(A, lda, strideA, Bm, ldb, strideB, Cm, ldc, strideC, M, N, K, blockIdx.x,
-                                    blockIdx.y, blockIdx.z, red);
+                                    blockIdx.y, blockIdx.z, threadIdx.x / WAVE, red);
 }
 
 // ----------------------------------------------------------------------------- expand
@@ -416,15 +417,16 @@ __device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const 
 
 // The fused g_x blocks and the g_w blocks in one launch: both depend only on the stacked
 // projection, and the g_w tiles fill the compute units the g_x strips leave free.
-// Blocks [0, ngx) are g_x (strip = id % nstrip, sample = id / nstrip); the rest are g_w
-// tiles (64 x 128, K split over the NW waves).
+// Blocks [0, ngx) are g_x (strip = id % nstrip, sample = id / nstrip); each of the rest
+// takes two g_w tiles (64 x 128) side by side, half of its waves on each with K split
+// over them, which halves the g_w blocks at the latency of one tile.
 template <class T, int MTA, int KS, int NW, int SW>
 __global__ __launch_bounds__(NW * WAVE) void bwd_tail_kernel(const T* __restrict__ Qgy, const T* __restrict__ w,
                                                              const T* __restrict__ At, int ldA, int R, int L,
                                                              int Cy, int Cx, T* __restrict__ gx, int nstrip,
                                                              int ngx, const T* __restrict__ Pgy,
                                                              const T* __restrict__ xhat, T* __restrict__ gw,
-                                                             int Kw, int gw_bx) {
+                                                             int Kw, int gw_bx, int gw_tiles) {
   __shared__ float red[NW][8][4][WAVE];
   __shared__ __attribute__((aligned(16))) GxShared<T, KS, SW> gs;
   const int id = blockIdx.x;
@@ -433,8 +435,12 @@ __global__ __launch_bounds__(NW * WAVE) void bwd_tail_kernel(const T* __restrict
                                        reinterpret_cast<float (*)[SW][4][WAVE]>(&red[0][0][0][0]), gs);
   } else {
     // g_w = sum_b (P gy_b)^T x_hat_b: M = Cy, N = Cx, K = B*Rx (A stored [K][Cy])
-    const int t = id - ngx;
-    gemm_block<T, true, 4, NW, 1>(Pgy, Cy, 0, xhat, Cx, 0, gw, Cx, 0, Cy, Cx, Kw, t % gw_bx, t / gw_bx, 0, red);
+    constexpr int HW = NW / 2;
+    const int half = threadIdx.x / (HW * WAVE);
+    const int t = 2 * (id - ngx) + half;
+    // a missing second tile still takes part in the barriers, with no columns
+    gemm_block<T, true, 4, HW, 1>(Pgy, Cy, 0, xhat, Cx, 0, gw, Cx, 0, Cy, t < gw_tiles ? Cx : 0, Kw, t % gw_bx,
+                                  t / gw_bx, 0, threadIdx.x / WAVE - half * HW, red + half * HW);
   }
 }
 
@@ -559,35 +565,39 @@ hipError_t launch_expand(bool bf16_io, const void* At, int ldA, const void* Bz, 
 
 template <class T, int MTA, int KS, int SW>
 static hipError_t bwd_tail_cfg(const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L, int Cy,
-                               int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw,
+                               int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw, int ncu,
                                hipStream_t st) {
   constexpr int NW = MTA == 1 ? 8 : 4;
   const int nstrip = (Cx + 16 * SW - 1) / (16 * SW);
   const int ngx = nstrip * B;
-  const int gw_bx = (Cx + 127) / 128, gw_by = (Cy + 63) / 64;
-  hipLaunchKernelGGL((bwd_tail_kernel<T, MTA, KS, NW, SW>), dim3(ngx + gw_bx * gw_by), dim3(NW * WAVE), 0, st,
+  const int gw_bx = (Cx + 127) / 128, gw_tiles = gw_bx * ((Cy + 63) / 64);
+  const int ngw = (gw_tiles + 1) / 2;
+  hipLaunchKernelGGL((bwd_tail_kernel<T, MTA, KS, NW, SW>), dim3(ngx + ngw), dim3(NW * WAVE), 0, st,
                      (const T*)Qgy, (const T*)w, (const T*)At, ldA, R, L, Cy, Cx, (T*)gx, nstrip, ngx, (const T*)Pgy,
-                     (const T*)xhat, (T*)gw, Kw, gw_bx);
+                     (const T*)xhat, (T*)gw, Kw, gw_bx, gw_tiles);
   return hipGetLastError();
 }
 
 template <class T, int MTA, int KS>
 static hipError_t bwd_tail_sw(const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L, int Cy,
-                              int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw,
+                              int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw, int ncu,
                               hipStream_t st) {
-  // 64-column strips when 128-column ones would leave compute units without a g_x block
-  if ((long)((Cx + 127) / 128) * B < 256 && Cx > 64)
-    return bwd_tail_cfg<T, MTA, KS, 4>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, st);
-  return bwd_tail_cfg<T, MTA, KS, 8>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, st);
+  // 64-column strips only when even they fit the compute units in one round: a second round
+  // of g_x blocks costs more than the wider strip's longer pass (measured on gfx950 at
+  // B = 32, C = 768: 11.2 us with 128-column strips against 14.7 us with 64-column ones)
+  if ((long)((Cx + 63) / 64) * B <= ncu && Cx > 64)
+    return bwd_tail_cfg<T, MTA, KS, 4>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, ncu, st);
+  return bwd_tail_cfg<T, MTA, KS, 8>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, ncu, st);
 }
 
 template <class T>
 static hipError_t bwd_tail_t(const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L, int Cy,
-                             int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw, hipStream_t st) {
+                             int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw, int ncu,
+                             hipStream_t st) {
   const int mta = (R + 15) / 16;
   const int ks = (R + MM<T>::KSTEP - 1) / MM<T>::KSTEP;
 #define BTC(MA, K) \
-  if (mta == MA && ks == K) return bwd_tail_sw<T, MA, K>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, st);
+  if (mta == MA && ks == K) return bwd_tail_sw<T, MA, K>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, ncu, st);
   if constexpr (MM<T>::KSTEP == 32) {
     BTC(1, 1) BTC(2, 1) BTC(3, 2) BTC(4, 2)
   } else {
@@ -598,10 +608,11 @@ static hipError_t bwd_tail_t(const void* Qgy, const void* w, const void* At, int
 }
 
 hipError_t launch_bwd_tail(bool bf16_io, const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L,
-                           int Cy, int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw,
+                           int Cy, int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw, int ncu,
                            hipStream_t st) {
-  return bf16_io ? bwd_tail_t<bf16>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, st)
-                 : bwd_tail_t<float>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, st);
+  if (ncu < 1) return hipErrorInvalidValue;
+  return bf16_io ? bwd_tail_t<bf16>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, ncu, st)
+                 : bwd_tail_t<float>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, ncu, st);
 }
 
 bool gx_fused_applies(bool bf16_io, int B, int Cx, int Cy) {

@@ -25,10 +25,11 @@ hipError_t launch_expand(bool bf16_io, const void* At, int ldA, const void* Bz, 
 
 // gx[b][l][c] = sum_r At[l][r] (sum_k Qgy[b][r][k] w[k][c]) with g_hat_x kept in LDS
 // (rounded to the I/O dtype), and g_w = sum_b Pgy_b^T xhat_b (Pgy [Kw][Cy], xhat [Kw][Cx],
-// Kw = B * Rx), in one launch. Applies when w is small enough to stay in L2.
+// Kw = B * Rx), in one launch. Applies when w is small enough to stay in L2. `ncu` is the
+// device's compute unit count, which sizes the grid.
 bool gx_fused_applies(bool bf16_io, int B, int Cx, int Cy);
 hipError_t launch_bwd_tail(bool bf16_io, const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L,
-                           int Cy, int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw,
+                           int Cy, int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw, int ncu,
                            hipStream_t st);
 
 // ---- calibration ([KD1], [KD2])

@@ -2,6 +2,8 @@
 the CPU oracle, with projections injected so the kernels are checked on their own.
 
 Every call goes through the C ABI (ctypes binding of libinstant.so)."""
+import zlib
+
 import numpy as np
 import pytest
 
@@ -70,6 +72,9 @@ RAGGED = [
     ("bf16", 3, 130, 392, 520, 64, 64),
     ("fp32", 2, 64, 64, 64, 64, 64),
     ("bf16", 7, 49, 448, 1792, 33, 31),
+    # more g_w tiles than the compute units the g_x strips leave free (256 of them): some
+    # blocks take two tiles, an odd count of them
+    ("bf16", 40, 33, 264, 2952, 5, 9),
 ]
 
 
@@ -78,7 +83,7 @@ def test_hot_path_ragged(case):
     from gpu_util import TOL, from_dev, rel
     dtype, B, L, Cx, Cy, Rx, Ry = case
     print(f"[hot path ragged] {case}", flush=True)
-    rng = np.random.default_rng(hash(case) % (2 ** 32))
+    rng = np.random.default_rng(zlib.crc32(repr(case).encode()))
     P = rng.standard_normal((Rx, L)) / np.sqrt(L)
     Q = rng.standard_normal((Ry, L)) / np.sqrt(L)
     x = W.to_io(rng.standard_normal((B, L, Cx)), dtype)
