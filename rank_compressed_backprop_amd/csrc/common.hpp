@@ -118,6 +118,19 @@ __device__ inline void store_row(T* __restrict__ p, const float v[W]) {
   *reinterpret_cast<typename VecW<T, W>::type*>(p) = o;
 }
 
+// The same with the non-temporal hint, for a large output that neither this launch nor the
+// next one reads: its lines then go on to memory while the launch runs instead of staying
+// dirty in L2 until the write-back at the launch's end (1.5 us of an 11 us launch that
+// writes 25 MB, measured on gfx950).
+template <class T, int W>
+__device__ inline void store_row_nt(T* __restrict__ p, const float v[W]) {
+  typedef typename VecW<T, W>::type vec;
+  vec o;
+#pragma unroll
+  for (int j = 0; j < W; ++j) o[j] = from_f32<T>(v[j]);
+  __builtin_nontemporal_store(o, reinterpret_cast<vec*>(p));
+}
+
 __device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 }  // namespace instant

@@ -281,7 +281,7 @@ __global__ __launch_bounds__(NW * WAVE) void expand_kernel(const T* __restrict__
           float o[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) o[j] = acc[j][v];
-          store_row<T, 8>(out + ((size_t)b * L + l) * C + col, o);
+          store_row_nt<T, 8>(out + ((size_t)b * L + l) * C + col, o);
         }
       }
     }
@@ -407,7 +407,7 @@ __device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const 
             float o[SW];
 #pragma unroll
             for (int j = 0; j < SW; ++j) o[j] = o4[j][v];
-            store_row<T, SW>(out + ((size_t)b * L + l) * Cx + col, o);
+            store_row_nt<T, SW>(out + ((size_t)b * L + l) * Cx + col, o);
           }
         }
       }
