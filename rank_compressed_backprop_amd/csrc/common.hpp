@@ -26,6 +26,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int WAVE = 64;
+// accelerator dies (XCDs) of the chip, each with its own L2; a launch's workgroups are dealt
+// to them in turn by workgroup id
+constexpr int XCDS = 8;
 
 template <class T> struct MM;
 

@@ -18,8 +18,9 @@ namespace instant {
 // panels (one panel for diagonal tiles). Stages go straight from memory to LDS
 // (global_load_lds, 16 bytes per lane) through a SYRK_STAGES-deep ring, so later stages'
 // loads are in flight while the matrix cores consume the oldest. Within a panel, 16-byte
-// chunk c of row r sits in slot c ^ wide_swz(r), which keeps the fragment reads of 8 (and
-// of 16) consecutive rows on distinct banks. Lanes whose row or channel is out of range
+// chunk c of row r sits in slot c ^ (r & 7): the fragment reads of 16 consecutive rows
+// then run at the full LDS rate (measured on gfx950; an extra flip of the slot for rows
+// 8-15 cost a quarter of it). Lanes whose row or channel is out of range
 // read a zeroed pad instead. Slices write float32 partial tiles (in fragment order); a
 // second kernel adds them to the float64 sums in slice order.
 constexpr int ST = 128;           // statistics tile edge
@@ -73,7 +74,7 @@ __device__ inline void wait_oldest_stage(int younger) {
 }
 
 constexpr int WPANEL = ST * 128;  // bytes per panel of a stage
-__device__ inline int wide_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ inline int slot_swz(int r) { return r & 7; }
 
 // NLD = 0: the four compute waves also stream the ring; NLD = 4 or 8: that many more waves
 // only stream it (a wave sustains about a sixth of a compute unit's L2 read bandwidth).
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(64 * (4 + NLD)) void syrk_kernel(SyrkSide s0, SyrkS
       for (int h = 0; h < HP; ++h) {
         const int j = HP * li + h;
         const int rloc = 8 * j + (lane >> 3);
-        const int chunk = (lane & 7) ^ wide_swz(rloc);
+        const int chunk = (lane & 7) ^ slot_swz(rloc);
         const int row = tb * ST + rloc;
         const int kk = k0 + chunk * EPC;
         const T* src = (row < L && kk < C) ? Xb + (size_t)row * C + kk : zpad;
@@ -175,8 +176,8 @@ __global__ __launch_bounds__(64 * (4 + NLD)) void syrk_kernel(SyrkSide s0, SyrkS
       for (int t = 0; t < 4; ++t) {
         const int ra = 64 * wr + 16 * t + (lane & 15);
         const int rb = 64 * wc + 16 * t + (lane & 15);
-        af[t] = *reinterpret_cast<const frag*>(pa + ra * 128 + 16 * ((4 * h + g) ^ wide_swz(ra)));
-        bf[t] = *reinterpret_cast<const frag*>(pb + rb * 128 + 16 * ((4 * h + g) ^ wide_swz(rb)));
+        af[t] = *reinterpret_cast<const frag*>(pa + ra * 128 + 16 * ((4 * h + g) ^ slot_swz(ra)));
+        bf[t] = *reinterpret_cast<const frag*>(pb + rb * 128 + 16 * ((4 * h + g) ^ slot_swz(rb)));
       }
 #pragma unroll
       for (int t = 0; t < 4; ++t)

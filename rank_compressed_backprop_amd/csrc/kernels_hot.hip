@@ -289,26 +289,31 @@ __global__ __launch_bounds__(NW * WAVE) void expand_kernel(const T* __restrict__
 }
 
 // ----------------------------------------------------------------------------- fused g_x
-// For layers whose weight stays resident in L2: block (strip, b) first forms
-// g_hat_x_b[:, strip] = Qgy_b (Ry x Cy) . w[:, strip] (Cy x 16*SW) on the matrix cores
-// (the NW waves split Cy, LDS sums them), keeps it in LDS in the I/O dtype, and then
-// expands g_x_b[:, strip] = Q^T g_hat_x_b[:, strip] over all L tokens. A lane owns SW
-// adjacent columns of the strip.
-template <class T, int KS, int SW>
+// For layers whose weight stays resident in L2: block (strip, sample group) first forms
+// g_hat_x_b[:, strip] = Qgy_b (Ry x Cy) . w[:, strip] (Cy x 16*SW) on the matrix cores for
+// the SPB samples b of its group at once (their Ry-row blocks of Qgy are adjacent, so they
+// stack into the 16-row A operand; the NW waves split Cy, LDS sums them), keeps them in
+// LDS in the I/O dtype, and then expands g_x_b[:, strip] = Q^T g_hat_x_b[:, strip] over
+// all L tokens, one Q^T fragment serving every sample. Stacking samples divides the w
+// strip a block streams from L2 by SPB at the same block count. A lane owns SW adjacent
+// columns of the strip.
+template <class T, int MTA, int KS, int SW>
 struct GxShared {
-  static constexpr int GROWS = KS * MM<T>::KSTEP;  // rows of the LDS operand (zero beyond R)
+  // rows of the LDS operand: the stacked g_hat_x rows, and the K padding of the last
+  // sample's expansion operand (zero)
+  static constexpr int GROWS = 16 * MTA > KS * MM<T>::KSTEP ? 16 * MTA : KS * MM<T>::KSTEP;
   T g[GROWS][16 * SW];
 };
 
-template <class T, int MTA, int KS, int NW, int SW>
+template <class T, int MTA, int KS, int NW, int SW, int SPB>
 __device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const T* __restrict__ w,
                                                const T* __restrict__ At, int ldA, int R, int L, int Cy, int Cx,
-                                               T* __restrict__ out, int strip, int b, float (*red)[SW][4][WAVE],
-                                               GxShared<T, KS, SW>& gs) {
+                                               T* __restrict__ out, int strip, int b0, int nb,
+                                               float (*red)[SW][4][WAVE], GxShared<T, MTA, KS, SW>& gs) {
   typedef MM<T> mm;
   typedef typename mm::frag frag;
   constexpr int U = 3;  // with 8 waves, the 24 k-steps of Cy = 768 in one round of loads
-  constexpr int GROWS = GxShared<T, KS, SW>::GROWS;
+  constexpr int GROWS = GxShared<T, MTA, KS, SW>::GROWS;
   constexpr int SC = 16 * SW;  // strip columns
   auto& gsm = gs.g;
   const int lane = threadIdx.x & (WAVE - 1);
@@ -317,11 +322,12 @@ __device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const 
   const int col = strip * SC + lc;
   const bool col_ok = col < Cx;
   const int kl = mm::G * (lane >> 4);
-  const T* __restrict__ Ab = Qgy + (size_t)b * R * Cy;
+  const T* __restrict__ Ab = Qgy + (size_t)b0 * R * Cy;
+  const int rows = nb * R;  // stacked g_hat_x rows of the group
 
   for (int e = threadIdx.x; e < GROWS * SC; e += NW * WAVE) (&gsm[0][0])[e] = (T)0.0f;
 
-  // phase 1: g_hat_x tile
+  // phase 1: g_hat_x tiles of the group
   f32x4 acc[MTA][SW];
 #pragma unroll
   for (int t = 0; t < MTA; ++t)
@@ -339,7 +345,7 @@ __device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const 
 #pragma unroll
       for (int t = 0; t < MTA; ++t) {
         const int m = 16 * t + (lane & 15);
-        af[u][t] = load_frag<T>(Ab + (size_t)m * Cy + k0, m < R && s < nsteps && k0 + mm::G <= Cy);
+        af[u][t] = load_frag<T>(Ab + (size_t)m * Cy + k0, m < rows && s < nsteps && k0 + mm::G <= Cy);
       }
     }
 #pragma unroll
@@ -358,7 +364,7 @@ __device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const 
     __syncthreads();
     for (int v = wave; v < 4; v += NW) {
       const int r = 16 * t + 4 * (lane >> 4) + v;
-      if (r < R) {
+      if (r < rows) {
 #pragma unroll
         for (int j = 0; j < SW; ++j) {
           float sum = red[0][j][v][lane];
@@ -372,10 +378,13 @@ __device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const 
   }
 
   // phase 2: expand over all tokens; each wave takes every NW-th 16-token tile
-  frag bz[KS][SW];
+  frag bz[SPB][KS][SW];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) load_strip_T<T, SW>(&gsm[0][0], SC, ks * mm::KSTEP + kl, R, lc, true, bz[ks]);
-  constexpr int MPW = 4;
+  for (int g = 0; g < SPB; ++g)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      load_strip_T<T, SW>(&gsm[g * R][0], SC, ks * mm::KSTEP + kl, g < nb ? R : 0, lc, true, bz[g][ks]);
+  constexpr int MPW = SPB == 1 ? 4 : 2;
   const int ntl = (L + 15) / 16;
   for (int tl0 = wave; tl0 < ntl; tl0 += NW * MPW) {
     frag af[MPW][KS];
@@ -392,22 +401,26 @@ __device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const 
       const int tl = tl0 + i * NW;
       if (tl >= ntl) break;
       const int l0 = 16 * tl;
-      f32x4 o4[SW];
 #pragma unroll
-      for (int j = 0; j < SW; ++j) o4[j] = zero4();
+      for (int g = 0; g < SPB; ++g) {
+        if (g >= nb) break;
+        f32x4 o4[SW];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+        for (int j = 0; j < SW; ++j) o4[j] = zero4();
 #pragma unroll
-        for (int j = 0; j < SW; ++j) o4[j] = mm::mma(af[i][ks], bz[ks][j], o4[j]);
-      if (col_ok) {
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int l = l0 + 4 * (lane >> 4) + v;
-          if (l < L) {
-            float o[SW];
+          for (int j = 0; j < SW; ++j) o4[j] = mm::mma(af[i][ks], bz[g][ks][j], o4[j]);
+        if (col_ok) {
 #pragma unroll
-            for (int j = 0; j < SW; ++j) o[j] = o4[j][v];
-            store_row_nt<T, SW>(out + ((size_t)b * L + l) * Cx + col, o);
+          for (int v = 0; v < 4; ++v) {
+            const int l = l0 + 4 * (lane >> 4) + v;
+            if (l < L) {
+              float o[SW];
+#pragma unroll
+              for (int j = 0; j < SW; ++j) o[j] = o4[j][v];
+              store_row_nt<T, SW>(out + ((size_t)(b0 + g) * L + l) * Cx + col, o);
+            }
           }
         }
       }
@@ -417,22 +430,31 @@ __device__ __forceinline__ void gx_fused_block(const T* __restrict__ Qgy, const 
 
 // The fused g_x blocks and the g_w blocks in one launch: both depend only on the stacked
 // projection, and the g_w tiles fill the compute units the g_x strips leave free.
-// Blocks [0, ngx) are g_x (strip = id % nstrip, sample = id / nstrip); each of the rest
+// Blocks [0, ngx) are g_x (one strip and a group of SPB samples each); each of the rest
 // takes two g_w tiles (64 x 128) side by side, half of its waves on each with K split
 // over them, which halves the g_w blocks at the latency of one tile.
-template <class T, int MTA, int KS, int NW, int SW>
+template <class T, int MTA, int KS, int NW, int SW, int SPB>
 __global__ __launch_bounds__(NW * WAVE) void bwd_tail_kernel(const T* __restrict__ Qgy, const T* __restrict__ w,
-                                                             const T* __restrict__ At, int ldA, int R, int L,
-                                                             int Cy, int Cx, T* __restrict__ gx, int nstrip,
-                                                             int ngx, const T* __restrict__ Pgy,
+                                                             const T* __restrict__ At, int ldA, int B, int R,
+                                                             int L, int Cy, int Cx, T* __restrict__ gx,
+                                                             int nstrip, int ngx, const T* __restrict__ Pgy,
                                                              const T* __restrict__ xhat, T* __restrict__ gw,
                                                              int Kw, int gw_bx, int gw_tiles) {
   __shared__ float red[NW][8][4][WAVE];
-  __shared__ __attribute__((aligned(16))) GxShared<T, KS, SW> gs;
+  __shared__ __attribute__((aligned(16))) GxShared<T, MTA, KS, SW> gs;
   const int id = blockIdx.x;
   if (id < ngx) {
-    gx_fused_block<T, MTA, KS, NW, SW>(Qgy, w, At, ldA, R, L, Cy, Cx, gx, id % nstrip, id / nstrip,
-                                       reinterpret_cast<float (*)[SW][4][WAVE]>(&red[0][0][0][0]), gs);
+    // Workgroups are dealt to the XCDs in turn (id % 8). Units in strip-major order, a
+    // contiguous run of them per XCD, so that each XCD's L2 holds one or two strips of w
+    // rather than all of it.
+    const int per = ngx / XCDS;
+    const int unit = id < per * XCDS ? (id % XCDS) * per + id / XCDS : id;
+    const int ngroups = ngx / nstrip;
+    const int strip = unit / ngroups;
+    const int b0 = SPB * (unit % ngroups);
+    gx_fused_block<T, MTA, KS, NW, SW, SPB>(Qgy, w, At, ldA, R, L, Cy, Cx, gx, strip, b0,
+                                            min(SPB, B - b0),
+                                            reinterpret_cast<float (*)[SW][4][WAVE]>(&red[0][0][0][0]), gs);
   } else {
     // g_w = sum_b (P gy_b)^T x_hat_b: M = Cy, N = Cx, K = B*Rx (A stored [K][Cy])
     constexpr int HW = NW / 2;
@@ -563,18 +585,18 @@ hipError_t launch_expand(bool bf16_io, const void* At, int ldA, const void* Bz, 
                  : expand_t<float>(At, ldA, Bz, B, R, L, C, out, st);
 }
 
-template <class T, int MTA, int KS, int SW>
+template <class T, int MTA, int KS, int SW, int SPB>
 static hipError_t bwd_tail_cfg(const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L, int Cy,
-                               int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw, int ncu,
+                               int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw,
                                hipStream_t st) {
   constexpr int NW = MTA == 1 ? 8 : 4;
   const int nstrip = (Cx + 16 * SW - 1) / (16 * SW);
-  const int ngx = nstrip * B;
+  const int ngx = nstrip * ((B + SPB - 1) / SPB);
   const int gw_bx = (Cx + 127) / 128, gw_tiles = gw_bx * ((Cy + 63) / 64);
   const int ngw = (gw_tiles + 1) / 2;
-  hipLaunchKernelGGL((bwd_tail_kernel<T, MTA, KS, NW, SW>), dim3(ngx + ngw), dim3(NW * WAVE), 0, st,
-                     (const T*)Qgy, (const T*)w, (const T*)At, ldA, R, L, Cy, Cx, (T*)gx, nstrip, ngx, (const T*)Pgy,
-                     (const T*)xhat, (T*)gw, Kw, gw_bx, gw_tiles);
+  hipLaunchKernelGGL((bwd_tail_kernel<T, MTA, KS, NW, SW, SPB>), dim3(ngx + ngw), dim3(NW * WAVE), 0, st,
+                     (const T*)Qgy, (const T*)w, (const T*)At, ldA, B, R, L, Cy, Cx, (T*)gx, nstrip, ngx,
+                     (const T*)Pgy, (const T*)xhat, (T*)gw, Kw, gw_bx, gw_tiles);
   return hipGetLastError();
 }
 
@@ -582,12 +604,18 @@ template <class T, int MTA, int KS>
 static hipError_t bwd_tail_sw(const void* Qgy, const void* w, const void* At, int ldA, int B, int R, int L, int Cy,
                               int Cx, void* gx, const void* Pgy, const void* xhat, void* gw, int Kw, int ncu,
                               hipStream_t st) {
+  if constexpr (MTA == 1) {
+    // two samples stacked in the 16-row tile: half the w strip per sample, in 64-column
+    // strips so that the block count stays that of one sample in 128-column strips
+    if (2 * R <= 16 && B > 1 && Cx > 64)
+      return bwd_tail_cfg<T, 1, KS, 4, 2>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, st);
+  }
   // 64-column strips only when even they fit the compute units in one round: a second round
   // of g_x blocks costs more than the wider strip's longer pass (measured on gfx950 at
   // B = 32, C = 768: 11.2 us with 128-column strips against 14.7 us with 64-column ones)
   if ((long)((Cx + 63) / 64) * B <= ncu && Cx > 64)
-    return bwd_tail_cfg<T, MTA, KS, 4>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, ncu, st);
-  return bwd_tail_cfg<T, MTA, KS, 8>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, ncu, st);
+    return bwd_tail_cfg<T, MTA, KS, 4, 1>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, st);
+  return bwd_tail_cfg<T, MTA, KS, 8, 1>(Qgy, w, At, ldA, B, R, L, Cy, Cx, gx, Pgy, xhat, gw, Kw, st);
 }
 
 template <class T>
