@@ -55,7 +55,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="bert_attn")
+    ap.add_argument("--workload", default="bert_attn",
+                    help="bert_attn (the headline line) or bert_block (every linear layer of a BERT-base "
+                         "encoder layer: its low-rank backward against the exact one)")
     ap.add_argument("--batches", type=int, default=32,
                     help="distinct resident batches cycled through (more than N_cal, so consecutive "
                          "calibration windows see different statistics)")
@@ -73,6 +75,10 @@ def main():
         print("bench.py measures one GPU only: the multi-GPU data-parallel path is a design, not built "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "bert_block":
+        bench_block(args)
+        return
 
     import numpy as np
     import torch
@@ -244,6 +250,107 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
     print(json.dumps(out), flush=True)
+
+
+# The linear layers of one BERT-base encoder layer (B=32, L=512, bf16): the four attention
+# projections (Q, K, V and the output projection, 768 -> 768 each; a fused QKV is the first
+# three side by side) and the FFN (768 -> 3072 -> 768), each with its own P and Q.
+BLOCK_LAYERS = (("q", "bert_attn", 0, 0), ("k", "bert_attn", 0, 1), ("v", "bert_attn", 0, 2),
+                ("o", "bert_attn", 0, 3), ("ffn_up", "bert_ffn", "up", 0), ("ffn_down", "bert_ffn", "down", 0))
+
+
+def bench_block(args):
+    """Per training step of a BERT-base encoder layer's linear layers: the INSTANT path
+    (forward compression + low-rank backward of every layer) against the exact backward
+    (g_x = g_y w and g_w = g_y^T x by PyTorch/hipBLASLt GEMMs), with the formula FLOP ratio
+    and the activation memory ratio of notes 关键设计 3 (vanilla backward 4 L Cx Cy per sample;
+    low-rank 2 (Rx + Ry)(Cx Cy + L Cx + L Cy), the compression included; kept activation
+    x [L, Cx] against x_hat [Rx, Cx]). Calibration is set-up here, on 4 batches per layer."""
+    import numpy as np
+    import torch
+
+    import rank_compressed_backprop_amd as rcb
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    n_setup, layers = 4, []
+    for name, wname, lname, k in BLOCK_LAYERS:
+        wl = W.get_workload(wname)
+        ly = wl.layer(lname)
+        B, L = wl.B, wl.L
+        lay = rcb.InstantLayer(rcb.make_config(L, ly.Cx, ly.Cy, B, R_max=64, p=wl.p, N_t=wl.n_t, eps=wl.eps,
+                                               dtype="bf16", comp="paper"), device=dev)
+        for t in range(n_setup):
+            d = W.make_layer_batch(wl, lname, 200 * k + t)
+            s = lay.calibrate(up(d["x"]), up(d["gy"]), B, finalize=(t == n_setup - 1))
+            if s != rcb.INSTANT_OK:
+                raise RuntimeError(f"{name}: calibration failed: " + rcb.instant_status_str(s))
+        d = W.make_layer_batch(wl, lname, 200 * k + n_setup)
+        _, info = lay.query()
+        layers.append({"name": name, "lay": lay, "B": B, "L": L, "Cx": ly.Cx, "Cy": ly.Cy,
+                       "Rx": info.Rx, "Ry": info.Ry, "x": up(d["x"]), "gy": up(d["gy"]),
+                       "w": up(W.to_io(W.make_w(wl, lname), "bf16")),
+                       "xhat": torch.empty((B, info.Rx, ly.Cx), dtype=torch.bfloat16, device=dev),
+                       "gw": torch.empty((ly.Cy, ly.Cx), dtype=torch.bfloat16, device=dev),
+                       "gx": torch.empty((B, L, ly.Cx), dtype=torch.bfloat16, device=dev)})
+        del d
+    st = torch.cuda.current_stream()
+
+    def ev_time(fn, reps=50):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(reps):
+            fn()
+        e1.record(st)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3  # us
+
+    def instant(c):
+        c["lay"].compress_fwd(c["x"], c["B"], c["xhat"])
+        c["lay"].backward(c["xhat"], c["gy"], c["w"], c["B"], c["gw"], c["gx"])
+
+    def exact(c):
+        gy2 = c["gy"].view(-1, c["Cy"])
+        torch.mm(gy2, c["w"], out=c["gx"].view(-1, c["Cx"]))
+        torch.mm(gy2.t(), c["x"].view(-1, c["Cx"]), out=c["gw"])
+
+    out_layers, tot = [], {"instant_us": 0.0, "exact_us": 0.0, "flops_vanilla": 0, "flops_lowrank": 0,
+                           "act_bytes_exact": 0, "act_bytes_instant": 0}
+    for c in layers:
+        ti, te = ev_time(lambda: instant(c)), ev_time(lambda: exact(c))
+        B, L, Cx, Cy, Rx, Ry = c["B"], c["L"], c["Cx"], c["Cy"], c["Rx"], c["Ry"]
+        fv = B * 4 * L * Cx * Cy
+        fl = B * 2 * (Rx + Ry) * (Cx * Cy + L * Cx + L * Cy)
+        ax, ah = 2 * B * L * Cx, 2 * B * Rx * Cx
+        out_layers.append({"layer": c["name"], "Cx": Cx, "Cy": Cy, "Rx": Rx, "Ry": Ry, "instant_us": ti,
+                           "exact_us": te, "speedup": te / ti, "flop_ratio": fv / fl, "activation_ratio": ax / ah})
+        for key, v in (("instant_us", ti), ("exact_us", te), ("flops_vanilla", fv), ("flops_lowrank", fl),
+                       ("act_bytes_exact", ax), ("act_bytes_instant", ah)):
+            tot[key] += v
+    both = lambda: [instant(c) for c in layers]  # noqa: E731
+    t_block = ev_time(both)
+    B, L = layers[0]["B"], layers[0]["L"]
+    res = {"metric": "BERT-base encoder layer, all linear layers: low-rank backward time (compression "
+                     "included) against the exact backward",
+           "value": B * L / (t_block * 1e-6), "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "BERT-base encoder layer linears Q, K, V, O (768->768), FFN up (768->3072), "
+                                  "down (3072->768); B=32 L=512; calibrated on 4 synthetic batches per layer",
+                      "global_batch": B, "seq_len": L},
+           "block": {"instant_us": t_block, "instant_us_sum_of_layers": tot["instant_us"],
+                     "exact_us": tot["exact_us"], "speedup": tot["exact_us"] / t_block,
+                     "flop_ratio_formula": tot["flops_vanilla"] / tot["flops_lowrank"],
+                     "activation_memory_ratio": tot["act_bytes_exact"] / tot["act_bytes_instant"]},
+           "layers": out_layers}
+    print(json.dumps(res), flush=True)
 
 
 def cpu_baseline(wl, nsample):
