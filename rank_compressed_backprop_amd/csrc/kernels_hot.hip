@@ -537,12 +537,19 @@ template <class T, bool AT>
 static hipError_t gemm_t(const void* A, int lda, size_t sA, const void* Bm, int ldb, size_t sB, void* Cm, int ldc,
                          size_t sC, int batch, int M, int N, int K, hipStream_t st) {
   const int nsteps = (K + MM<T>::KSTEP - 1) / MM<T>::KSTEP;
+  constexpr bool BF = MM<T>::KSTEP == 32;
   if constexpr (AT) {
+    // bf16 at K = B*R = 448 (BERT FFN): two waves with four steps in flight each beat four
+    // waves with two (11.6 against 14.3 us on gfx950)
+    if (BF && nsteps < 32) return gemm_cfg<T, true, 4, 2, 4>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
     if (nsteps >= 8) return gemm_cfg<T, true, 4, 4, 2>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
     return gemm_cfg<T, true, 4, 2, 2>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
   } else {
-    // skinny M: split K over eight waves so each issues few rounds of loads
-    if (nsteps >= 16) return gemm_cfg<T, false, 2, 8, 2>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
+    // skinny M: split K over eight waves so each issues few rounds of loads; in bf16 only
+    // for long K (measured on gfx950 at M = 448: 16.7 against 21.0 us at K = 3072, but
+    // 13.7 against 9.6 us at K = 768)
+    if (nsteps >= (BF ? 64 : 16))
+      return gemm_cfg<T, false, 2, 8, 2>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
     return gemm_cfg<T, false, 2, 4, 2>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
   }
 }
