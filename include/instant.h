@@ -36,7 +36,13 @@
  *     bfloat16. Accumulation is float32; statistics are summed in float64 across
  *     batches.
  *   - Cx and Cy must be multiples of 8; 1 <= L <= 2048; 1 <= R_max <= 64 and R_max <= L.
- *   - A handle is used from one stream at a time; calls are not re-entrant.
+ *   - Calls on one handle are not re-entrant (one host thread at a time). They are
+ *     ordered by their streams: the caller gives every call its inputs on that call's
+ *     stream. One overlap is allowed: statistics calls (instant_calibrate) may run on a
+ *     second stream while instant_compress_fwd / instant_backward run on another, since
+ *     they use disjoint parts of the workspace. A finalizing call rewrites the inactive
+ *     projection buffer, the one the calls before the previous finalize used: order it
+ *     after the hot-path calls already enqueued on the other stream (an event).
  */
 #ifndef INSTANT_H_
 #define INSTANT_H_
