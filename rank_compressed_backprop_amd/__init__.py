@@ -186,7 +186,12 @@ class InstantLayer:
             self.h = None
 
     def __del__(self):
-        self.close()
+        # at interpreter shutdown the module's globals may already be gone; the process
+        # exit releases the handle then
+        try:
+            self.close()
+        except TypeError:
+            pass
 
     def _check(self, s, where):
         if s != INSTANT_OK:
