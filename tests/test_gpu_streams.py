@@ -40,7 +40,8 @@ def _run(two_streams: bool, xs, gys, w, P0, Q0, L, Cx, Cy, B):
             side.wait_event(ev)
         s = lay.calibrate(xs[t], gys[t], B, finalize=fin, stream=side)
         assert s == rcb.INSTANT_OK, rcb.instant_status_str(s)
-        outs.append((gw, gx, xhat[:, :Rx]))
+        # x_hat is packed [B, Rx, Cx] at the start of the R_max-sized buffer
+        outs.append((gw, gx, xhat.view(-1)[:B * Rx * Cx].view(B, Rx, Cx)))
     torch.cuda.synchronize()
     _, info = lay.query()
     P = torch.empty((info.Rx, L), device="cuda")
