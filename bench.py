@@ -28,6 +28,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
+MFMA_FP32_PEAK_TFLOPS = 157.3   # MI355X dense fp32
+WORKLOAD_NAMES = {"tiny": "tiny fp32", "bert_attn": "BERT-base attention projection",
+                  "bert_ffn": "BERT-base FFN", "effformer": "EfficientFormer-L1 last-stage",
+                  "llm_mlp": "LLM MLP"}
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "proj_bert_attn_traffic.json")
 
 
@@ -56,11 +61,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="bert_attn",
-                    help="bert_attn (the headline line) or bert_block (every linear layer of a BERT-base "
-                         "encoder layer: its low-rank backward against the exact one)")
-    ap.add_argument("--batches", type=int, default=32,
-                    help="distinct resident batches cycled through (more than N_cal, so consecutive "
-                         "calibration windows see different statistics)")
+                    help="bert_attn (the headline line); bert_block (every linear layer of a BERT-base "
+                         "encoder layer: its low-rank backward against the exact one); or one layer of "
+                         "tiny, bert_ffn, effformer, llm_mlp run through the same step loop")
+    ap.add_argument("--layer", default="0", help="layer of a two-layer workload (up or down)")
+    ap.add_argument("--batches", type=int, default=None,
+                    help="distinct resident batches cycled through (default 32: more than N_cal, so "
+                         "consecutive calibration windows see different statistics; N_cal for llm_mlp, "
+                         "whose batches take seconds each to generate)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--one-stream", action="store_true",
                     help="run the statistics on the main stream too (no overlap with the hot path)")
@@ -89,7 +97,9 @@ def main():
     import workloads as W
 
     wl = W.get_workload(args.workload)
-    ly = wl.layer(0)
+    layer = int(args.layer) if args.layer.isdigit() else args.layer
+    ly = wl.layer(layer)
+    li = wl.layers.index(ly)
     B, L, Cx, Cy = wl.B, wl.L, ly.Cx, ly.Cy
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -101,13 +111,16 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     # resident synthetic batches (distinct, so the 256 MB last-level cache cannot hold a step's data)
-    nb = max(args.batches, wl.n_cal)
+    nb = args.batches if args.batches is not None else (wl.n_cal if L * (Cx + Cy) * B > 1 << 27 else 32)
+    nb = max(nb, wl.n_cal)
     xs, gys = [], []
     for t in range(nb):
-        d = W.make_layer_batch(wl, 0, t)
+        d = W.make_layer_batch(wl, li, t)
         xs.append(up(d["x"]))
         gys.append(up(d["gy"]))
-    w = up(W.to_io(W.make_w(wl, 0), wl.dtype))
+        if nb * B * L * (Cx + Cy) > 1 << 30:
+            print(f"[bench] generated resident batch {t + 1}/{nb}", file=sys.stderr, flush=True)
+    w = up(W.to_io(W.make_w(wl, li), wl.dtype))
     del d
 
     R_max = 64
@@ -215,14 +228,18 @@ def main():
     bytes_fwd = es * (B * L * Cx + B * Rx * Cx)
     bytes_bwd = es * (B * L * Cy + B * Rx * Cx + 2 * Cx * Cy + B * L * Cx)
     flops_bwd = B * (2 * (Rx + Ry) * L * Cy + 2 * (Rx + Ry) * Cx * Cy + 2 * Ry * L * Cx)
+    # statistics: the upper triangle of both L x L sums per batch (the mirror earns no credit)
+    flops_acc = L * (L + 1) * B * (Cx + Cy)
     gbs_fwd = bytes_fwd / t_fwd / 1e9
 
+    headline = wl.name == "bert_attn"
     ms_per_step = wall / args.steps * 1e3
     tokens = args.steps * B * L
     value = tokens / wall
 
     out = {
-        "metric": "low-rank backward tokens/s + achieved HBM GB/s (% peak), BERT-base linear",
+        "metric": ("low-rank backward tokens/s + achieved HBM GB/s (% peak), BERT-base linear" if headline else
+                   f"low-rank backward tokens/s + achieved HBM GB/s (% peak), {wl.name} linear"),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -234,7 +251,8 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": f"BERT-base attention projection linear, B={B} L={L} Cx={Cx} Cy={Cy}, "
+        "config": {"workload": f"{WORKLOAD_NAMES.get(wl.name, wl.name)} linear{'' if len(wl.layers) == 1 else ' (' + ly.name + ')'}, "
+                               f"B={B} L={L} Cx={Cx} Cy={Cy}, "
                                f"eps={wl.eps} p={wl.p} N_cal={wl.n_cal} N_t={wl.n_t}",
                    "global_batch": B, "seq_len": L, "parallelism": "single GPU",
                    "step": "compress + low-rank backward every step; statistics on the first N_cal steps of "
@@ -247,6 +265,11 @@ def main():
             "backward_pct_hbm_peak": 100.0 * bytes_bwd / t_bwd / 1e9 / HBM_PEAK_GBS,
             "backward_tokens_per_s": B * L / t_bwd, "backward_TFLOPs": flops_bwd / t_bwd / 1e12,
             "statistics_per_batch_us": t_acc * 1e6,
+            "statistics_TFLOPs": flops_acc / t_acc / 1e12,
+            "statistics_pct_mfma_bf16_peak" if wl.dtype == "bf16" else "statistics_pct_mfma_fp32_peak":
+                100.0 * flops_acc / t_acc / 1e12 / (MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else
+                                                    MFMA_FP32_PEAK_TFLOPS),
+            "statistics_GBs": es * B * L * (Cx + Cy) / t_acc / 1e9,
             "finalize_ms": t_fin * 1e3,
             "finalize_in_loop_ms": (sum(fin_loop) / len(fin_loop) * 1e3) if fin_loop else None,
             "finalizes_in_loop": len(fin_loop), "host_enqueue_us_per_plain_step": t_issue * 1e6, "jacobi_sweeps": [info2.sweeps_x, info2.sweeps_g],
@@ -259,7 +282,7 @@ def main():
                      "algorithmic_bytes_per_launch": bytes_fwd},
     }
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and headline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
     print(json.dumps(out), flush=True)
 

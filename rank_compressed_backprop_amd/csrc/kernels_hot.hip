@@ -538,18 +538,37 @@ static hipError_t gemm_t(const void* A, int lda, size_t sA, const void* Bm, int 
                          size_t sC, int batch, int M, int N, int K, hipStream_t st) {
   const int nsteps = (K + MM<T>::KSTEP - 1) / MM<T>::KSTEP;
   constexpr bool BF = MM<T>::KSTEP == 32;
+  const long strips = (N + 127) / 128;
   if constexpr (AT) {
-    // bf16 at K = B*R = 448 (BERT FFN): two waves with four steps in flight each beat four
-    // waves with two (11.6 against 14.3 us on gfx950)
-    if (BF && nsteps < 32) return gemm_cfg<T, true, 4, 2, 4>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
+    if constexpr (BF) {
+      // (bf16, measured on gfx950) Many 64x128 tiles (g_w of an LLM MLP: 5504 at 11008 x 4096,
+      // K = 272): one wave per tile with the whole K in three rounds of loads, 76.8 us against
+      // 122 us for two waves splitting K. Few tiles (BERT FFN, 288 at K = 448; EfficientFormer,
+      // 112 at K = 3712): four waves split K, 10.8-11.4 us against 12.0-12.5 us with two, and
+      // 34 us against 57 us at the long K with two steps in flight per wave.
+      const long tiles = strips * ((M + 63) / 64);
+      if (tiles >= 2048) return gemm_cfg<T, true, 4, 1, 3>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
+      if (nsteps <= 16) return gemm_cfg<T, true, 4, 4, 1>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
+      return gemm_cfg<T, true, 4, 4, 2>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
+    }
     if (nsteps >= 8) return gemm_cfg<T, true, 4, 4, 2>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
     return gemm_cfg<T, true, 4, 2, 2>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
   } else {
-    // skinny M: split K over eight waves so each issues few rounds of loads; in bf16 only
-    // for long K (measured on gfx950 at M = 448: 16.7 against 21.0 us at K = 3072, but
-    // 13.7 against 9.6 us at K = 768)
-    if (nsteps >= (BF ? 64 : 16))
-      return gemm_cfg<T, false, 2, 8, 2>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
+    if constexpr (BF) {
+      // (bf16, measured on gfx950) Eight waves split K; every row block streams its own pass
+      // over the B strip, so the tallest row blocks that still give at least 192 blocks win:
+      // LLM MLP (M = 272, K = 11008) 48 rows, 75 us against 114 us with 32 rows; BERT FFN down
+      // (M = 448, K = 768) 48 rows, 9.1 us against 10.0 us; BERT FFN up (N = 768, K = 3072)
+      // 16 rows, 13.8 against 16.8 us; EfficientFormer (M = 3712, N = 448) 64 rows, 18.4 us
+      // against 19.7 us.
+      auto blocks = [&](int mt) { return strips * ((M + 16 * mt - 1) / (16 * mt)); };
+      if (blocks(4) >= 192) return gemm_cfg<T, false, 4, 8, 1>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
+      if (blocks(3) >= 192) return gemm_cfg<T, false, 3, 8, 1>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
+      if (blocks(2) >= 192) return gemm_cfg<T, false, 2, 8, 1>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
+      return gemm_cfg<T, false, 1, 8, 2>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
+    }
+    // fp32 (the eigensolver's warm start W = C V): K split over eight waves for long K
+    if (nsteps >= 16) return gemm_cfg<T, false, 2, 8, 2>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
     return gemm_cfg<T, false, 2, 4, 2>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
   }
 }
