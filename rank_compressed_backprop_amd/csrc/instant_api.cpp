@@ -23,15 +23,39 @@ using namespace instant;
 constexpr int MAX_L = 2048;  // a Jacobi pair stages 16 columns of L floats in LDS
 constexpr int MAX_R = 64;
 constexpr int LD_QT = 64;
-constexpr int SYRK_TARGET_BLOCKS = 256;  // one 128x128 tile-slice per compute unit
+constexpr int SYRK_TARGET_BLOCKS = 4096;  // tile-slices of a batch's statistics (both sides)
+constexpr int SYRK_MIN_STAGES = 16;      // shortest slice: the LDS ring's fill stays small
 constexpr int SYRK_MAX_SPLIT = 64;
 constexpr int SYRK_TILE = 128;
 
 inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
-inline int syrk_split_cap(int L) {
-  const int nt = syrk_tiles(L);
-  return std::max(1, std::min(SYRK_MAX_SPLIT, (SYRK_TARGET_BLOCKS + nt - 1) / nt));
+// K slices of one statistic's SYRK for a batch of B samples. Both statistics get slices of
+// about the same length (the launch holds both, and its time is that of its longest
+// blocks), long enough to amortise the ring's fill, short enough to give about
+// SYRK_TARGET_BLOCKS tile-slices per batch so that the last round of blocks is short.
+// Counts of 8 or more are multiples of 8: slice s then stays on accelerator die s % 8 and
+// the row panels of its K range are shared in that die's L2 by every tile (measured on
+// gfx950 at L = 2048, B = 8, C = 4096 / 11008: 8 / 24 slices 578 us, 4 / 11 slices
+// 802 us, 2 / 2 slices 1037 us). The count depends only on the layer's shapes and B, not
+// on which statistics a call carries, so split and joint calls sum identically.
+int syrk_nsplit(const instant_config& c, int B, int C) {
+  const int kstep = c.dtype == INSTANT_BF16 ? 32 : 16;
+  auto stages = [&](int ch) { return (long)B * (((ch + kstep - 1) / kstep + 1) / 2); };  // two k-steps a stage
+  const long work = (long)syrk_tiles(c.L) * (stages(c.Cx) + stages(c.Cy));
+  const long len = std::max<long>(SYRK_MIN_STAGES, (work + SYRK_TARGET_BLOCKS - 1) / SYRK_TARGET_BLOCKS);
+  const long st = stages(C);
+  long n = (st + len / 2) / len;
+  if (n >= 8) n = (n + 4) / 8 * 8;
+  n = std::min<long>(std::min<long>(n, SYRK_MAX_SPLIT), st);
+  return (int)std::max<long>(1, n);
+}
+
+// The most slices one statistic takes at any batch size up to B_max (sizes its partials).
+int syrk_split_max(const instant_config& c, int C) {
+  int m = 1;
+  for (int b = 1; b <= c.B_max; ++b) m = std::max(m, syrk_nsplit(c, b, C));
+  return m;
 }
 
 bool config_ok(const instant_config* c) {
@@ -49,7 +73,8 @@ bool config_ok(const instant_config* c) {
 }
 
 struct Layout {
-  size_t SX, SG, zpad, part, eig, sig_x, sig_g, info, rank, P32[2], Q32[2], PQ[2], Qt[2], Pgy, Qgy, gxh, total;
+  size_t SX, SG, zpad, part, part_x_tiles, eig, sig_x, sig_g, info, rank, P32[2], Q32[2], PQ[2], Qt[2], Pgy, Qgy,
+      gxh, total;
   int ldL;
 };
 
@@ -67,7 +92,9 @@ Layout layout_of(const instant_config* c) {
   l.SX = take(L * L * sizeof(double));
   l.SG = take(L * L * sizeof(double));
   l.zpad = take(256);
-  l.part = take(2 * (size_t)syrk_split_cap(c->L) * syrk_tiles(c->L) * SYRK_TILE * SYRK_TILE * sizeof(float));
+  l.part_x_tiles = (size_t)syrk_split_max(*c, c->Cx) * syrk_tiles(c->L);
+  l.part = take((l.part_x_tiles + (size_t)syrk_split_max(*c, c->Cy) * syrk_tiles(c->L)) * SYRK_TILE * SYRK_TILE *
+                sizeof(float));
   l.eig = take(eig_workspace_bytes(c->L));
   l.sig_x = take(L * sizeof(float));
   l.sig_g = take(L * sizeof(float));
@@ -105,7 +132,7 @@ struct instant_layer {
   double* SG() const { return (double*)(ws + lay.SG); }
   // partial tiles of the statistics' split reduction, one region per statistic
   float* part(int side) const {
-    return (float*)(ws + lay.part) + (size_t)side * syrk_split_cap(cfg.L) * syrk_tiles(cfg.L) * SYRK_TILE * SYRK_TILE;
+    return (float*)(ws + lay.part) + (side ? lay.part_x_tiles * SYRK_TILE * SYRK_TILE : 0);
   }
   int* info_dev() const { return (int*)(ws + lay.info); }
   int* rank_dev() const { return (int*)(ws + lay.rank); }
@@ -120,24 +147,13 @@ namespace {
 inline hipStream_t S(void* stream) { return (hipStream_t)stream; }
 inline instant_status hip_ok(hipError_t e) { return e == hipSuccess ? INSTANT_OK : INSTANT_E_HIP; }
 
-int syrk_nsplit(const instant_layer* h, int B, int C) {
-  const int kstep = h->bf16 ? 32 : 16;
-  const int stages = ((C + kstep - 1) / kstep + 1) / 2;  // two k-steps per ring stage
-  const long total = (long)B * stages;
-  // slices of at least 16 stages (the LDS pipeline's fill is then small), enough of them
-  // to give every compute unit a tile-slice, a multiple of 8 when there are 16 or more
-  int nsplit = (int)std::min<long>(syrk_split_cap(h->cfg.L), std::max<long>(1, total / 16));
-  if (nsplit >= 16) nsplit -= nsplit % 8;
-  return nsplit;
-}
-
 // Both statistics of a batch (either input may be NULL) in one SYRK launch.
 instant_status accumulate(instant_layer* h, const void* x, const void* gy, int B, hipStream_t st) {
   SyrkSide sides[2];
   int n = 0;
   // the first batch of a window overwrites the sums, so a finalize need not clear them
-  if (x) sides[n++] = SyrkSide{x, h->cfg.Cx, syrk_nsplit(h, B, h->cfg.Cx), h->part(0), h->SX(), h->nx == 0};
-  if (gy) sides[n++] = SyrkSide{gy, h->cfg.Cy, syrk_nsplit(h, B, h->cfg.Cy), h->part(1), h->SG(), h->ng == 0};
+  if (x) sides[n++] = SyrkSide{x, h->cfg.Cx, syrk_nsplit(h->cfg, B, h->cfg.Cx), h->part(0), h->SX(), h->nx == 0};
+  if (gy) sides[n++] = SyrkSide{gy, h->cfg.Cy, syrk_nsplit(h->cfg, B, h->cfg.Cy), h->part(1), h->SG(), h->ng == 0};
   return hip_ok(launch_syrk(h->bf16, sides, n, B, h->cfg.L, h->ws + h->lay.zpad, st));
 }
 
