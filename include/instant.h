@@ -75,6 +75,19 @@ typedef enum { INSTANT_FP32 = 0, INSTANT_BF16 = 1 } instant_dtype;
  * with P = c * U_R^T. */
 typedef enum { INSTANT_COMP_PAPER = 0, INSTANT_COMP_NONE = 1, INSTANT_COMP_RATIO = 2 } instant_comp;
 
+/* Eigensolver of the finalize ([KD1]: "SVD of C"; [KD2]: only the top k + p directions
+ * and E = sum_i sigma_i^2 = ||C||_F^2 are needed).
+ *   JACOBI    the full decomposition: blocked one-sided Jacobi on all L columns, warm
+ *             started from the previous finalize's rotation.
+ *   SUBSPACE  the top m = R_max + 16 (rounded up to 16) eigenpairs by sub_iters steps of
+ *             block subspace iteration with Rayleigh-Ritz (W = C V on the matrix cores,
+ *             one-sided Jacobi on the m columns), warm started from the previous
+ *             finalize's basis; E is taken from C. Status E_RANK when eps * E lies beyond
+ *             the m directions, E_NOCONV when a kept direction's Ritz residual exceeds
+ *             3e-5 * sigma_0. When m >= L it is the JACOBI solver. sigma_x / sigma_g
+ *             then hold the m leading values followed by zeros. */
+typedef enum { INSTANT_SOLVER_JACOBI = 0, INSTANT_SOLVER_SUBSPACE = 1 } instant_solver;
+
 typedef struct {
   int32_t L;          /* tokens per sample */
   int32_t Cx, Cy;     /* input / output channels */
@@ -85,7 +98,9 @@ typedef struct {
   float eps;          /* energy threshold, 0 < eps <= 1 ([KD2]) */
   int32_t dtype;      /* instant_dtype of x, gy, w, xhat, gw, gx */
   int32_t comp;       /* instant_comp */
-  int32_t max_sweeps; /* Jacobi sweep limit (e.g. 30) */
+  int32_t max_sweeps; /* Jacobi sweep limit (e.g. 30); per subspace step for SUBSPACE */
+  int32_t solver;     /* instant_solver */
+  int32_t sub_iters;  /* subspace steps per finalize (SUBSPACE; >= 1) */
 } instant_config;
 
 typedef struct {

@@ -36,13 +36,15 @@ INSTANT_OK, INSTANT_E_ARG, INSTANT_E_SHAPE, INSTANT_E_STATE, INSTANT_E_RANK = 0,
 INSTANT_E_ENERGY, INSTANT_E_NONFINITE, INSTANT_E_NOCONV, INSTANT_E_HIP = 5, 6, 7, 8
 INSTANT_FP32, INSTANT_BF16 = 0, 1
 INSTANT_COMP_PAPER, INSTANT_COMP_NONE, INSTANT_COMP_RATIO = 0, 1, 2
+INSTANT_SOLVER_JACOBI, INSTANT_SOLVER_SUBSPACE = 0, 1
 
 
 class instant_config(ctypes.Structure):
     _fields_ = [("L", ctypes.c_int32), ("Cx", ctypes.c_int32), ("Cy", ctypes.c_int32),
                 ("B_max", ctypes.c_int32), ("R_max", ctypes.c_int32), ("p", ctypes.c_int32),
                 ("N_t", ctypes.c_int32), ("eps", ctypes.c_float), ("dtype", ctypes.c_int32),
-                ("comp", ctypes.c_int32), ("max_sweeps", ctypes.c_int32)]
+                ("comp", ctypes.c_int32), ("max_sweeps", ctypes.c_int32), ("solver", ctypes.c_int32),
+                ("sub_iters", ctypes.c_int32)]
 
 
 class instant_info(ctypes.Structure):
@@ -157,12 +159,14 @@ def instant_get_statistics(h, C_X, C_G, stream=None) -> int:
 # ----------------------------------------------------------------------------- handle owner
 
 def make_config(L, Cx, Cy, B_max, R_max=64, p=2, N_t=100, eps=0.95, dtype="bf16", comp="paper",
-                max_sweeps=30) -> instant_config:
+                max_sweeps=30, solver="jacobi", sub_iters=6) -> instant_config:
     dt = {"fp32": INSTANT_FP32, "bf16": INSTANT_BF16}[dtype] if isinstance(dtype, str) else int(dtype)
     cp = {"paper": INSTANT_COMP_PAPER, "none": INSTANT_COMP_NONE, "ratio": INSTANT_COMP_RATIO}[comp] \
         if isinstance(comp, str) else int(comp)
+    sv = {"jacobi": INSTANT_SOLVER_JACOBI, "subspace": INSTANT_SOLVER_SUBSPACE}[solver] \
+        if isinstance(solver, str) else int(solver)
     return instant_config(int(L), int(Cx), int(Cy), int(B_max), int(min(R_max, L)), int(p), int(N_t),
-                          float(eps), dt, cp, int(max_sweeps))
+                          float(eps), dt, cp, int(max_sweeps), sv, int(sub_iters))
 
 
 class InstantLayer:

@@ -69,6 +69,8 @@ bool config_ok(const instant_config* c) {
   if (c->dtype != INSTANT_FP32 && c->dtype != INSTANT_BF16) return false;
   if (c->comp < INSTANT_COMP_PAPER || c->comp > INSTANT_COMP_RATIO) return false;
   if (c->max_sweeps < 1) return false;
+  if (c->solver != INSTANT_SOLVER_JACOBI && c->solver != INSTANT_SOLVER_SUBSPACE) return false;
+  if (c->solver == INSTANT_SOLVER_SUBSPACE && c->sub_iters < 1) return false;
   return true;
 }
 
@@ -253,8 +255,12 @@ INSTANT_API instant_status instant_calibrate(instant_layer* h, const void* x, co
                            hh->Qt(tl.t), LD_QT, st);
   };
   int flags[EIG_HOST_FLAGS];
-  hipError_t e = run_eig(h->SX(), h->SG(), 1.0 / (double)h->nx, 1.0 / (double)h->ng, h->cfg.L, h->cfg.max_sweeps,
-                         h->warm, h->ws + h->lay.eig, out, flags, st);
+  const int m = h->cfg.solver == INSTANT_SOLVER_SUBSPACE ? eig_subspace_width(h->cfg.L, h->cfg.R_max) : 0;
+  hipError_t e = m > 0 ? run_eig_subspace(h->SX(), h->SG(), 1.0 / (double)h->nx, 1.0 / (double)h->ng, h->cfg.L, m,
+                                          h->cfg.sub_iters, h->cfg.max_sweeps, h->warm, h->ws + h->lay.eig, out,
+                                          flags, st)
+                       : run_eig(h->SX(), h->SG(), 1.0 / (double)h->nx, 1.0 / (double)h->ng, h->cfg.L,
+                                 h->cfg.max_sweeps, h->warm, h->ws + h->lay.eig, out, flags, st);
   if (e != hipSuccess) {
     h->warm = false;
     return INSTANT_E_HIP;
@@ -287,8 +293,10 @@ INSTANT_API instant_status instant_calibrate(instant_layer* h, const void* x, co
     I.generation += 1;
   }
   h->last = status;
-  // a failed decomposition may leave the accumulated rotation unusable: restart cold
-  h->warm = (status == INSTANT_OK || status == INSTANT_E_RANK);
+  // a failed decomposition may leave the accumulated rotation unusable: restart cold (a
+  // subspace basis that has not converged yet is still the best start for the next one)
+  h->warm = (status == INSTANT_OK || status == INSTANT_E_RANK) ||
+            (m > 0 && status == INSTANT_E_NOCONV);
   h->nx = h->ng = 0;
   return status;
 }

@@ -72,6 +72,7 @@ constexpr int F_NALIVE = 18;    // [2] columns above the noise floor
 constexpr int F_BARRIER2 = 20;  // Gram check arrivals
 constexpr int F_INFO = 24;      // [2][INFO_WORDS] copy of each side's info block
 constexpr int F_GMAX = 40;      // [3 slots][2 sides] Gram check maxima (float bits)
+constexpr int F_EEXACT = 48;    // 2 doubles: ||C||_F^2 per side from the statistic (subspace solver)
 constexpr size_t EIG_FLAGS_BYTES = 256;
 
 struct EigBufs {
@@ -83,6 +84,7 @@ struct EigBufs {
   int* flags;
   int* version;     // [2][nb]
   int* cols[2];     // [ncols] column order: columns above the noise floor first
+  float* res[2];    // subspace solver: Ritz residual ||C v_c - sigma_c v_c|| per column
 };
 
 static EigBufs eig_bufs(void* work, const EigLayout& e) {
@@ -115,12 +117,16 @@ static EigBufs eig_bufs(void* work, const EigLayout& e) {
   b.cols[0] = (int*)p;
   p += e.colbytes;
   b.cols[1] = (int*)p;
+  p += e.colbytes;
+  b.res[0] = (float*)p;
+  p += e.nrmbytes;
+  b.res[1] = (float*)p;
   return b;
 }
 
 size_t eig_workspace_bytes(int L) {
   const EigLayout e = eig_layout(L);
-  return 6 * e.wbytes + 2 * e.vbytes + 2 * e.nrmbytes + EIG_FLAGS_BYTES + e.verbytes + 2 * e.colbytes;
+  return 6 * e.wbytes + 2 * e.vbytes + 4 * e.nrmbytes + EIG_FLAGS_BYTES + e.verbytes + 2 * e.colbytes;
 }
 
 // ---------------------------------------------------------------------------- set-up kernels
@@ -186,7 +192,7 @@ __global__ __launch_bounds__(64) void colnorm_kernel(EigSides a, int ldw, int L)
 // rotated). cols = [columns above the floor in index order, then the others]; n_alive
 // counts the first group. One block of 1024 threads per side (blockIdx.x), ncols <= 2048.
 __global__ __launch_bounds__(1024) void frob_alive_kernel(EigSides a, double* __restrict__ scale_out, int L,
-                                                          int ncols, int* __restrict__ n_alive_out) {
+                                                          int ncols, int* __restrict__ n_alive_out, double noise_rel) {
   __shared__ int flag[2048];
   __shared__ int sum[1024];
   __shared__ double fro[1024];
@@ -207,7 +213,7 @@ __global__ __launch_bounds__(1024) void frob_alive_kernel(EigSides a, double* __
   }
   const double scale = fro[0];
   if (tid == 0) scale_out[side] = scale;
-  const double floor_g = NOISE_REL * scale;
+  const double floor_g = noise_rel * scale;
   // two columns per thread (ncols <= 2048)
   int f[2], own = 0;
 #pragma unroll
@@ -264,6 +270,8 @@ struct JacobiArgs {
   const int* cols[2];   // column order per side (alive columns first)
   const int* n_alive;   // [2]
   int L, ldw, nb, max_sweeps;
+  int nc;               // columns of W whose final norms are written (L, or the subspace width)
+  double noise_rel;     // columns under noise_rel * scale are neither rotated nor counted
   float tol, rot_tol;
 };
 
@@ -311,7 +319,7 @@ __device__ void jacobi_pair(const JacobiArgs& a, int side, int ba, int bb, int s
   double* __restrict__ Vg = a.V[side];
   if (threadIdx.x < 16) sm.col[threadIdx.x] = a.cols[side][(threadIdx.x < 8 ? ba : bb) * JB + (threadIdx.x & 7)];
   __syncthreads();
-  const double floor_g = NOISE_REL * a.scale[side];
+  const double floor_g = a.noise_rel * a.scale[side];
 
   // stage the columns, every load issued before any is used
   {
@@ -517,7 +525,7 @@ __device__ void gram_check_tile(const JacobiArgs& a, int side, int ti, int tj, J
   sm.npart[1][wave * 4 + (lane >> 4)][lane & 15] = sb;
   __syncthreads();
   if (wave == 0) {
-    const double floor_g = NOISE_REL * a.scale[side];
+    const double floor_g = a.noise_rel * a.scale[side];
     float m = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -666,12 +674,12 @@ __global__ __launch_bounds__(JT) void jacobi_kernel(JacobiArgs a) {
     }
     __syncthreads();  // sm.ok is rewritten in the next sweep
   }
-  // Final column norms of both sides (sigma = ||W[:, c]||, c < L): every block passed the
+  // Final column norms of both sides (sigma = ||W[:, c]||, c < nc): every block passed the
   // last sweep barrier, so W is complete; one wave per column.
   if (!aborted) {
     const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
-    for (int q = blockIdx.x * JW + wave; q < 2 * a.L; q += gridDim.x * JW) {
-      const int s = q / a.L, c = q - s * a.L;
+    for (int q = blockIdx.x * JW + wave; q < 2 * a.nc; q += gridDim.x * JW) {
+      const int s = q / a.nc, c = q - s * a.nc;
       const float* __restrict__ col = a.W[s] + (size_t)c * a.ldw;
       float acc = 0.0f;
       for (int r = lane; r < a.L; r += WAVE) acc += col[r] * col[r];
@@ -705,6 +713,10 @@ struct TruncArgs {
   int* info[2];
   float eps;
   int p, comp, R_max;
+  int n;                // column norms to rank: L (full decomposition) or the subspace width
+  const double* E_ext;  // [2] total energy ||C||_F^2 when only n < L values are known, else null
+  const float* res[2];  // Ritz residuals of the n columns (subspace solver), else null
+  float res_tol;        // largest residual of a kept direction, relative to sigma_0
 };
 
 __global__ __launch_bounds__(1024) void truncate_build_kernel(TruncArgs a, int ldw, int L, int* __restrict__ flags) {
@@ -724,10 +736,11 @@ __global__ __launch_bounds__(1024) void truncate_build_kernel(TruncArgs a, int l
   __shared__ int sk, sR, sstatus, kfirst;
   __shared__ float sc;
   const int tid = threadIdx.x;
+  const int n = a.n;  // ranked entries (the spectrum beyond them is known only through E)
   int Lp2 = 1;
-  while (Lp2 < L) Lp2 <<= 1;
+  while (Lp2 < n) Lp2 <<= 1;
   for (int i = tid; i < Lp2; i += 1024) {
-    key[i] = i < L ? nrm[i] : -1.0f;  // padding sorts last
+    key[i] = i < n ? nrm[i] : -1.0f;  // padding sorts last
     idx[i] = i;
   }
   __syncthreads();
@@ -752,13 +765,13 @@ __global__ __launch_bounds__(1024) void truncate_build_kernel(TruncArgs a, int l
       __syncthreads();
     }
   }
-  for (int i = tid; i < L; i += 1024) sigma_out[i] = key[i];
+  for (int i = tid; i < L; i += 1024) sigma_out[i] = i < n ? key[i] : 0.0f;
 
   // float64 prefix of sigma^2 in sorted order: thread t owns entries 2t and 2t+1 and the
   // block scans the pair sums (pre[i] = sum_{j <= i} sigma_j^2)
   {
-    const double a0 = 2 * tid < L ? (double)key[2 * tid] * (double)key[2 * tid] : 0.0;
-    const double a1 = 2 * tid + 1 < L ? (double)key[2 * tid + 1] * (double)key[2 * tid + 1] : 0.0;
+    const double a0 = 2 * tid < n ? (double)key[2 * tid] * (double)key[2 * tid] : 0.0;
+    const double a1 = 2 * tid + 1 < n ? (double)key[2 * tid + 1] * (double)key[2 * tid + 1] : 0.0;
     scan[tid] = a0 + a1;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
@@ -768,13 +781,13 @@ __global__ __launch_bounds__(1024) void truncate_build_kernel(TruncArgs a, int l
       __syncthreads();
     }
     const double before = scan[tid] - (a0 + a1);
-    if (2 * tid < L) pre[2 * tid] = before + a0;
-    if (2 * tid + 1 < L) pre[2 * tid + 1] = before + a0 + a1;
-    if (tid == 0) kfirst = L;
+    if (2 * tid < n) pre[2 * tid] = before + a0;
+    if (2 * tid + 1 < n) pre[2 * tid + 1] = before + a0 + a1;
+    if (tid == 0) kfirst = n;
     __syncthreads();
     // k = the smallest j with pre[j - 1] >= eps * E
-    const double thr = (double)eps * pre[L - 1];
-    for (int i = tid; i < L; i += 1024)
+    const double thr = (double)eps * (a.E_ext ? a.E_ext[side] : pre[n - 1]);
+    for (int i = tid; i < n; i += 1024)
       if (pre[i] >= thr && (i == 0 || pre[i - 1] < thr)) atomicMin(&kfirst, i);
     __syncthreads();
   }
@@ -783,21 +796,29 @@ __global__ __launch_bounds__(1024) void truncate_build_kernel(TruncArgs a, int l
     int status = 0;
     if (flags[F_BAD + side]) status = 6;        // non-finite statistics
     else if (!flags[F_CONV + side]) status = 7;  // no convergence
-    const double E = pre[L - 1];
+    const double E = a.E_ext ? a.E_ext[side] : pre[n - 1];
     int k = 0;
     double Sk = 0.0, SR = 0.0;
     if (status == 0 && !(E > 0.0)) status = (E == 0.0) ? 5 : 6;
     if (status == 0) {
-      if (kfirst < L) {
+      if (kfirst < n) {
         k = kfirst + 1;
         Sk = pre[kfirst];
-      } else {  // rounding made the total fall short of eps*E: only possible at eps == 1
+      } else if (!a.E_ext) {  // rounding made the total fall short of eps*E: only possible at eps == 1
         k = L;
         Sk = E;
+      } else {  // the energy threshold lies beyond the n directions the subspace holds
+        status = 4;
       }
     }
     int R = k + p < L ? k + p : L;
-    if (status == 0 && R > R_max) status = 4;
+    if (status == 0 && (R > R_max || R > n)) status = 4;
+    if (status == 0 && a.res[side]) {
+      // every kept direction must be an eigenvector to the residual tolerance
+      float worst = 0.0f;
+      for (int r = 0; r < R; ++r) worst = fmaxf(worst, a.res[side][idx[r]]);
+      if (!(worst <= a.res_tol * key[0])) status = 7;
+    }
     float c = 1.0f;
     if (status == 0) {
       SR = pre[R - 1];
@@ -902,7 +923,8 @@ hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv
     hipLaunchKernelGGL(identity_kernel, dim3(e.ncols, 2), dim3(256), 0, st, sd, e.ldw);
   }
   hipLaunchKernelGGL(colnorm_kernel, dim3(L, 2), dim3(64), 0, st, sd, e.ldw, L);
-  hipLaunchKernelGGL(frob_alive_kernel, dim3(2), dim3(1024), 0, st, sd, scale, L, e.ncols, flags + F_NALIVE);
+  hipLaunchKernelGGL(frob_alive_kernel, dim3(2), dim3(1024), 0, st, sd, scale, L, e.ncols, flags + F_NALIVE,
+                     NOISE_REL);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   JacobiArgs ja;
@@ -927,6 +949,8 @@ hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv
   ja.ldw = e.ldw;
   ja.nb = e.nb;
   ja.max_sweeps = max_sweeps;
+  ja.nc = L;
+  ja.noise_rel = NOISE_REL;
   // fp32 Gram entries carry a relative rounding error of about sqrt(L) * 2^-24
   ja.tol = fmaxf(1e-6f, 8.0f * sqrtf((float)e.ldw) * 5.96e-8f);
   ja.rot_tol = 0.25f * ja.tol;
@@ -950,6 +974,10 @@ hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv
   ta.p = out.p;
   ta.comp = out.comp;
   ta.R_max = out.R_max;
+  ta.n = L;
+  ta.E_ext = nullptr;
+  ta.res[0] = ta.res[1] = nullptr;
+  ta.res_tol = 0.0f;
   hipLaunchKernelGGL(truncate_build_kernel, dim3(2), dim3(1024), 0, st, ta, e.ldw, L, flags);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   // work that depends on the outcome is queued by the caller before this read-back
@@ -962,5 +990,213 @@ hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv
 }
 
 int eig_max_L() { return JAC_MAX_LDW; }
+
+// ---------------------------------------------------------------------------- subspace solver
+// Only the leading eigenpairs decide P and Q: the truncation needs the top k + p of them,
+// and the total energy E = ||C||_F^2 comes from C itself (关键设计 2 states the identity
+// sum_i sigma_i^2 = ||C||_F^2). Block subspace iteration keeps an L x m basis V (m a little
+// above R_max) and repeats
+//     W = C V                      (float32 matrix cores)
+//     W J = U Sigma                (the one-sided Jacobi above on the m columns)
+//     V <- U
+// The Jacobi step is the Rayleigh-Ritz step of this iteration: it diagonalises
+// (C V)^T (C V) = V^T C^2 V, whose Ritz vectors are those of C since C is PSD, and it
+// orthonormalises the basis. V J is the old basis in the Ritz coordinates, so
+// sigma_c ||u_c - (V J)_c|| = ||C (V J)_c - sigma_c (V J)_c|| is the residual of the Ritz
+// pair, which the truncation bounds for every kept direction. The basis of one
+// finalize starts the next; the first starts from pseudo-random columns.
+
+constexpr float SUB_RES_TOL = 3e-5f;  // kept Ritz residuals, relative to sigma_0
+constexpr double SUB_NOISE_REL = 1e-30;  // only columns without energy stay out of the rotations
+
+int eig_subspace_width(int L, int R_max) {
+  const int m = (R_max + 16 + 15) / 16 * 16;  // 16 more directions than the largest rank, whole blocks
+  return m < L ? m : 0;                        // 0: the subspace would be the whole space
+}
+
+// ||C||_F^2 = sum_i C_ii^2 + 2 sum_{i<j} C_ij^2 from the float64 upper-triangle sums, in a
+// fixed order (one block per side).
+__global__ __launch_bounds__(1024) void stat_frob_kernel(EigSides a, int L, double* __restrict__ out) {
+  __shared__ double part[1024];
+  const int side = blockIdx.x;
+  const double* S = a.S[side];
+  const double inv = a.inv[side];
+  double acc = 0.0;
+  for (int i = 0; i < L; ++i) {
+    const double* row = S + (size_t)i * L;
+    for (int j = i + threadIdx.x; j < L; j += 1024) {
+      const double v = row[j] * inv;
+      acc += (j == i ? 1.0 : 2.0) * v * v;
+    }
+  }
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int st = 512; st > 0; st >>= 1) {
+    if (threadIdx.x < st) part[threadIdx.x] += part[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[side] = part[0];
+}
+
+// Pseudo-random starting basis (a counter-based hash of row, column and side, uniform in
+// [-1, 1)), zero in the padding rows.
+__global__ __launch_bounds__(256) void seed_basis_kernel(EigSides a, int L, int ldw) {
+  const int c = blockIdx.x, s = blockIdx.y;
+  for (int r = threadIdx.x; r < ldw; r += 256) {
+    unsigned h = (unsigned)(r + 1) * 0x9E3779B1u ^ (unsigned)(c + 1) * 0x85EBCA77u ^ (unsigned)(s + 1) * 0xC2B2AE3Du;
+    h ^= h >> 15;
+    h *= 0x2C1B3C6Du;
+    h ^= h >> 12;
+    h *= 0x297A2D39u;
+    h ^= h >> 15;
+    a.V32[s][(size_t)c * ldw + r] = r < L ? (float)(h >> 8) * (2.0f / 16777216.0f) - 1.0f : 0.0f;
+  }
+}
+
+// Before each Jacobi launch: clear its counters, maxima and outputs, keep the statistics'
+// non-finite flags, the exact energies and an abort (a later launch then ends at once and
+// the host sees it); copy the basis to the float64 matrix the Jacobi rotates along with W.
+__global__ __launch_bounds__(256) void sub_reset_kernel(EigSides a, int* __restrict__ flags, int* __restrict__ version,
+                                                        int nver, int ldw) {
+  const int c = blockIdx.x, s = blockIdx.y;
+  if (c == 0 && s == 0) {
+    for (int i = threadIdx.x; i < F_INFO; i += 256)
+      if (i != F_BAD && i != F_BAD + 1 && i != F_ABORT) flags[i] = 0;
+    for (int i = threadIdx.x; i < 6; i += 256) flags[F_GMAX + i] = 0;
+    for (int i = threadIdx.x; i < nver; i += 256) version[i] = 0;
+  }
+  for (int r = threadIdx.x; r < ldw; r += 256) a.V[s][(size_t)c * ldw + r] = (double)a.V32[s][(size_t)c * ldw + r];
+}
+
+// After each Jacobi launch: the new basis u_c = W[:, c] / sigma_c and the Ritz residual
+// sigma_c ||u_c - (V J)_c||.
+__global__ __launch_bounds__(256) void sub_normalize_kernel(EigSides a, float* res0, float* res1, int ldw) {
+  __shared__ double part[256];
+  const int c = blockIdx.x, s = blockIdx.y;
+  const float sig = a.nrm[s][c];
+  const float inv = sig > 0.0f ? 1.0f / sig : 0.0f;
+  double d2 = 0.0;
+  for (int r = threadIdx.x; r < ldw; r += 256) {
+    const float u = a.W[s][(size_t)c * ldw + r] * inv;
+    const double diff = (double)u - a.V[s][(size_t)c * ldw + r];
+    d2 += diff * diff;
+    a.V32[s][(size_t)c * ldw + r] = u;
+  }
+  part[threadIdx.x] = d2;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (threadIdx.x < st) part[threadIdx.x] += part[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) (s ? res1 : res0)[c] = sig * (float)sqrt(part[0]);
+}
+
+hipError_t run_eig_subspace(const double* SX, const double* SG, double inv_nx, double inv_ng, int L, int m,
+                            int iters, int max_sweeps, bool warm, void* work, const EigOut& out,
+                            int host_flags[EIG_HOST_FLAGS], hipStream_t st) {
+  if (L > JAC_MAX_LDW || m < 16 || m % 16 || m >= L || iters < 1) return hipErrorInvalidValue;
+  const EigLayout e = eig_layout(L);
+  const EigBufs b = eig_bufs(work, e);
+  int* flags = b.flags;
+  double* scale = (double*)(flags + F_SCALE);
+  double* eexact = (double*)(flags + F_EEXACT);
+  hipError_t err;
+  if ((err = launch_zero(flags, EIG_FLAGS_BYTES + e.verbytes, st)) != hipSuccess) return err;
+  EigSides sd;
+  sd.S[0] = SX;
+  sd.S[1] = SG;
+  sd.inv[0] = inv_nx;
+  sd.inv[1] = inv_ng;
+  for (int s = 0; s < 2; ++s) {
+    sd.Wp[s] = b.Wtmp[s];  // C in float32, kept for every iteration's product
+    sd.W[s] = b.W[s];
+    sd.V[s] = b.V[s];
+    sd.V32[s] = b.V32[s];  // the basis; its first m columns carry over between finalizes
+    sd.nrm[s] = b.nrm[s];
+    sd.cols[s] = b.cols[s];
+  }
+  hipLaunchKernelGGL(jacobi_prep_kernel, dim3(e.ncols, 2), dim3(256), 0, st, sd, L, e.ldw, 0, flags + F_BAD);
+  hipLaunchKernelGGL(stat_frob_kernel, dim3(2), dim3(1024), 0, st, sd, L, eexact);
+  if (!warm) hipLaunchKernelGGL(seed_basis_kernel, dim3(m, 2), dim3(256), 0, st, sd, L, e.ldw);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
+  const int nb = m / JB;  // even: m is a multiple of 16
+  JacobiArgs ja;
+  ja.W[0] = b.W[0];
+  ja.W[1] = b.W[1];
+  ja.V[0] = b.V[0];
+  ja.V[1] = b.V[1];
+  ja.scale = scale;
+  ja.offmax = (unsigned*)(flags + F_OFFMAX);
+  ja.out = flags + F_SWEEPS;
+  ja.nrm[0] = b.nrm[0];
+  ja.nrm[1] = b.nrm[1];
+  ja.barrier = flags + F_BARRIER;
+  ja.barrier2 = flags + F_BARRIER2;
+  ja.gmax = (unsigned*)(flags + F_GMAX);
+  ja.abort = flags + F_ABORT;
+  ja.version = b.version;
+  ja.cols[0] = b.cols[0];
+  ja.cols[1] = b.cols[1];
+  ja.n_alive = flags + F_NALIVE;
+  ja.L = L;
+  ja.ldw = e.ldw;
+  ja.nb = nb;
+  ja.nc = m;
+  // Every column with energy takes part: the basis must come out orthonormal, and a column
+  // left unrotated is not orthogonal to the others once normalised (its direction is then
+  // dominated by leakage along the leading eigenvectors).
+  ja.noise_rel = SUB_NOISE_REL;
+  ja.max_sweeps = max_sweeps;
+  ja.tol = fmaxf(1e-6f, 8.0f * sqrtf((float)e.ldw) * 5.96e-8f);
+  ja.rot_tol = 0.25f * ja.tol;
+  void* kargs[] = {&ja};
+  const size_t dyn = (size_t)16 * e.ldw * sizeof(float);
+  for (int it = 0; it < iters; ++it) {
+    hipLaunchKernelGGL(sub_reset_kernel, dim3(m, 2), dim3(256), 0, st, sd, flags, b.version, 2 * nb, e.ldw);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    // W[c][r] = sum_k V[k][c] C[k][r]: A = V^T [m][ldw] (k contiguous), B = C [k][r]
+    if ((err = launch_gemm(false, false, b.V32[0], e.ldw, (size_t)(b.V32[1] - b.V32[0]), b.Wtmp[0], e.ldw,
+                           (size_t)(b.Wtmp[1] - b.Wtmp[0]), b.W[0], e.ldw, (size_t)(b.W[1] - b.W[0]), 2, m, e.ldw,
+                           L, st)) != hipSuccess)
+      return err;
+    hipLaunchKernelGGL(colnorm_kernel, dim3(m, 2), dim3(64), 0, st, sd, e.ldw, L);
+    hipLaunchKernelGGL(frob_alive_kernel, dim3(2), dim3(1024), 0, st, sd, scale, m, m, flags + F_NALIVE,
+                       SUB_NOISE_REL);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    err = hipLaunchCooperativeKernel((const void*)jacobi_kernel, dim3(nb), dim3(JT), kargs, dyn, st);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(sub_normalize_kernel, dim3(m, 2), dim3(256), 0, st, sd, b.res[0], b.res[1], e.ldw);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+
+  TruncArgs ta;
+  for (int s = 0; s < 2; ++s) {
+    ta.W[s] = b.W[s];
+    ta.nrm[s] = b.nrm[s];
+    ta.res[s] = b.res[s];
+  }
+  ta.P32[0] = out.P32;
+  ta.P32[1] = out.Q32;
+  ta.sigma[0] = out.sigma_x;
+  ta.sigma[1] = out.sigma_g;
+  ta.info[0] = out.info_x;
+  ta.info[1] = out.info_g;
+  ta.eps = out.eps;
+  ta.p = out.p;
+  ta.comp = out.comp;
+  ta.R_max = out.R_max;
+  ta.n = m;
+  ta.E_ext = eexact;
+  ta.res_tol = SUB_RES_TOL;
+  hipLaunchKernelGGL(truncate_build_kernel, dim3(2), dim3(1024), 0, st, ta, e.ldw, L, flags);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (out.before_readback && (err = out.before_readback(out.ctx, st)) != hipSuccess) return err;
+  if ((err = hipMemcpyAsync(host_flags, flags, EIG_HOST_FLAGS * sizeof(int), hipMemcpyDeviceToHost, st)) != hipSuccess)
+    return err;
+  if ((err = hipStreamSynchronize(st)) != hipSuccess) return err;
+  if (host_flags[F_ABORT]) return hipErrorLaunchTimeOut;
+  return hipSuccess;
+}
 
 }  // namespace instant

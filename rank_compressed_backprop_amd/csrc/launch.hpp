@@ -76,6 +76,14 @@ constexpr int EIG_HOST_FLAGS = 40;
 constexpr int EIGF_SWEEPS = 6, EIGF_CONV = 8, EIGF_BAD = 10, EIGF_NALIVE = 18, EIGF_INFO = 24;
 size_t eig_workspace_bytes(int L);
 int eig_max_L();
+// Subspace width for the top-R solver (0 when it would span the whole space).
+int eig_subspace_width(int L, int R_max);
+// The same outputs from `iters` steps of block subspace iteration on an L x m basis; the
+// truncation takes E = ||C||_F^2 from the statistic and rejects (status 7) kept directions
+// whose Ritz residual exceeds its tolerance, and (status 4) thresholds beyond m directions.
+hipError_t run_eig_subspace(const double* SX, const double* SG, double inv_nx, double inv_ng, int L, int m,
+                            int iters, int max_sweeps, bool warm, void* work, const EigOut& out,
+                            int host_flags[EIG_HOST_FLAGS], hipStream_t st);
 hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv_ng, int L, int max_sweeps,
                    bool warm, void* work, const EigOut& out, int host_flags[EIG_HOST_FLAGS], hipStream_t st);
 

@@ -1,7 +1,8 @@
 """GPU parity at the LLM MLP size (B=8, L=2048, Cx=4096 -> Cy=11008, bf16, p=16) in the
 launch configuration the library uses for it.
 
-The oracle cannot form the full 2048 x 2048 statistics in seconds (16 TFLOP in
+Both eigensolvers (the full Jacobi and the top-m subspace iteration) run on the same
+batches. The oracle cannot form the full 2048 x 2048 statistics in seconds (16 TFLOP in
 float64), so the statistics are checked on sampled entries, each computed from its
 definition; the decomposition and truncation are checked by running the oracle's
 decomposition on the statistic the GPU accumulated (a float64 2048 x 2048 matrix);
@@ -28,6 +29,9 @@ def test_llm_mlp_calibration_and_backward():
           flush=True)
     lay = rcb.InstantLayer(rcb.make_config(L, ly.Cx, ly.Cy, B, R_max=64, p=wl.p, eps=wl.eps, dtype=wl.dtype,
                                            comp="paper"))
+    # the subspace eigensolver on the same batches (top m = 80 eigenpairs, 关键设计 2)
+    lay_s = rcb.InstantLayer(rcb.make_config(L, ly.Cx, ly.Cy, B, R_max=64, p=wl.p, eps=wl.eps, dtype=wl.dtype,
+                                             comp="paper", solver="subspace"))
     rng = np.random.default_rng(5)
     m = 256
     rows = np.concatenate([rng.integers(0, L, m), np.arange(0, L, L // 16)])
@@ -38,8 +42,10 @@ def test_llm_mlp_calibration_and_backward():
         d = W.make_layer_batch(wl, 0, t)
         ex_x += O.autocorr_entries([d["x64"]], rows, cols) * B
         ex_g += O.autocorr_entries([d["gy64"]], rows, cols) * B
-        assert lay.calibrate(to_dev(d["x"], wl.dtype), to_dev(d["gy"], wl.dtype), B, finalize=False) == 0
-        del d
+        xd, gd = to_dev(d["x"], wl.dtype), to_dev(d["gy"], wl.dtype)
+        assert lay.calibrate(xd, gd, B, finalize=False) == 0
+        assert lay_s.calibrate(xd, gd, B, finalize=False) == 0
+        del d, xd, gd
     n = wl.n_cal * B
     CX = torch.empty((L, L), dtype=torch.float64, device="cuda")
     CG = torch.empty((L, L), dtype=torch.float64, device="cuda")
@@ -51,8 +57,16 @@ def test_llm_mlp_calibration_and_backward():
         print(f"  sampled statistics max err {e:.2e} (of the largest diagonal)", flush=True)
         assert e < 1e-6
         assert np.array_equal(C, C.T)
+    import time
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     s = lay.calibrate(None, None, 0, finalize=True)
+    t1 = time.perf_counter()
     assert s == rcb.INSTANT_OK, rcb.instant_status_str(s)
+    s2 = lay_s.calibrate(None, None, 0, finalize=True)
+    t2 = time.perf_counter()
+    print(f"  cold finalize: jacobi {1e3 * (t1 - t0):.1f} ms, subspace {1e3 * (t2 - t1):.1f} ms", flush=True)
+    assert s2 == rcb.INSTANT_OK, rcb.instant_status_str(s2)
     _, info = lay.query()
     ox = O.calibrate_side(CX, wl.eps, wl.p, O.COMP_PAPER, 64)
     og = O.calibrate_side(CG, wl.eps, wl.p, O.COMP_PAPER, 64)
@@ -61,14 +75,23 @@ def test_llm_mlp_calibration_and_backward():
           flush=True)
     assert ox["margin"] >= 1e-5 and og["margin"] >= 1e-5
     assert (info.kx, info.Rx, info.ky, info.Ry) == (ox["k"], ox["R"], og["k"], og["R"])
+    _, info_s = lay_s.query()
+    print(f"  subspace k/R x {info_s.kx}/{info_s.Rx} g {info_s.ky}/{info_s.Ry}, kept energy "
+          f"{info_s.kept_x:.6f}/{info_s.kept_g:.6f} vs jacobi {info.kept_x:.6f}/{info.kept_g:.6f}", flush=True)
+    assert (info_s.kx, info_s.Rx, info_s.ky, info_s.Ry) == (ox["k"], ox["R"], og["k"], og["R"])
+    assert abs(info_s.kept_x - info.kept_x) < 1e-5 and abs(info_s.kept_g - info.kept_g) < 1e-5
     P_g = torch.empty((info.Rx, L), device="cuda")
     Q_g = torch.empty((info.Ry, L), device="cuda")
     lay.get_projections(P_g, Q_g)
     torch.cuda.synchronize()
-    for Pg, o in ((P_g, ox), (Q_g, og)):
+    P_s = torch.empty((info_s.Rx, L), device="cuda")
+    Q_s = torch.empty((info_s.Ry, L), device="cuda")
+    lay_s.get_projections(P_s, Q_s)
+    torch.cuda.synchronize()
+    for Pg, o, tag in ((P_g, ox, "jacobi"), (Q_g, og, "jacobi"), (P_s, ox, "subspace"), (Q_s, og, "subspace")):
         Pg = Pg.cpu().numpy().astype(np.float64)
         dproj = rel(Pg.T @ Pg, o["P"].T @ o["P"])
-        print(f"  projector distance {dproj:.2e} (gap {o['gap']:.1e})", flush=True)
+        print(f"  {tag} projector distance {dproj:.2e} (gap {o['gap']:.1e})", flush=True)
         assert dproj < 1e-3
 
     d = W.make_layer_batch(wl, 0, wl.n_cal, with_w=True)
