@@ -46,12 +46,16 @@ def test_workspace_bytes_validates_config():
     bad = [
         dict(L=0), dict(L=2049), dict(Cx=12), dict(Cy=0), dict(B_max=0), dict(R_max=65),
         dict(eps=0.0), dict(eps=1.5), dict(dtype=7), dict(comp=5), dict(max_sweeps=0), dict(p=-1),
+        dict(solver=2), dict(solver=-1), dict(solver=1, sub_iters=0),
     ]
     for change in bad:
         cfg = rcb.make_config(512, 768, 768, 32, R_max=64, p=2)
         for k, v in change.items():
             setattr(cfg, k, v)
         assert rcb.instant_workspace_bytes(cfg) == 0, change
+    # the subspace solver is a valid choice with at least one step, and needs no more memory
+    sub = rcb.make_config(512, 768, 768, 32, R_max=64, p=2, solver="subspace", sub_iters=1)
+    assert rcb.instant_workspace_bytes(sub) == n
     # R_max is clamped to L by make_config; the raw struct may not exceed L
     cfg = rcb.make_config(16, 8, 8, 1, R_max=64)
     assert cfg.R_max == 16
