@@ -80,6 +80,9 @@ def parse():
                     help="eigensolver of the finalize: the full Jacobi decomposition, or the top-m "
                          "subspace iteration")
     ap.add_argument("--sub-iters", type=int, default=6, help="subspace steps per finalize")
+    ap.add_argument("--sync-finalize", action="store_true",
+                    help="finalize synchronously (the host waits for the outcome) instead of queueing it "
+                         "and letting the next forward compression after it pick up the new projections")
     return ap.parse_args()
 
 
@@ -160,6 +163,7 @@ def main():
     # The finalizing calls inside the timed loop are bracketed by HIP events on the side
     # stream (one pair per window; the span includes that step's statistics batch and the
     # host round trip of the finalize).
+    finalize_mode = True if args.sync_finalize else "async"
     main_st = torch.cuda.current_stream()
     side_st = torch.cuda.Stream() if not args.one_stream else main_st
     fin_events = []
@@ -176,7 +180,7 @@ def main():
             if fin and timed:
                 ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 ev[0].record(side_st)
-            s = lay.calibrate(xs[t], gys[t], B, finalize=fin, stream=side_st)
+            s = lay.calibrate(xs[t], gys[t], B, finalize=(fin and finalize_mode), stream=side_st)
             if fin and timed:
                 ev[1].record(side_st)
                 fin_events.append(ev)
@@ -267,6 +271,8 @@ def main():
                    "step": "compress + low-rank backward every step; statistics on the first N_cal steps of "
                            "each N_t window; eigen-decomposition + truncation once per window",
                    "streams": "statistics and finalize on a side stream" if not args.one_stream else "one stream",
+                   "finalize": "synchronous" if args.sync_finalize else
+                               "asynchronous (new projections from the first forward after it completes)",
                    "Rx": Rx, "Ry": Ry, "kx": info.kx, "ky": info.ky},
         "parts": {
             "compress_fwd_us": t_fwd * 1e6, "compress_fwd_GBs": gbs_fwd,

@@ -88,6 +88,9 @@ typedef enum { INSTANT_COMP_PAPER = 0, INSTANT_COMP_NONE = 1, INSTANT_COMP_RATIO
  *             then hold the m leading values followed by zeros. */
 typedef enum { INSTANT_SOLVER_JACOBI = 0, INSTANT_SOLVER_SUBSPACE = 1 } instant_solver;
 
+/* The finalize argument of instant_calibrate. */
+typedef enum { INSTANT_FINALIZE_NONE = 0, INSTANT_FINALIZE_SYNC = 1, INSTANT_FINALIZE_ASYNC = 2 } instant_finalize;
+
 typedef struct {
   int32_t L;          /* tokens per sample */
   int32_t Cx, Cy;     /* input / output channels */
@@ -132,9 +135,21 @@ instant_status instant_destroy(instant_layer* h);
  * finalize != 0 then turns both sums into means over the samples seen, takes the
  * eigen-decomposition of each, truncates at the energy threshold with p extra
  * bases, applies the compensation ([KD2]), publishes the new P and Q and clears
- * the sums. A finalize needs samples on both sides (else E_STATE). It returns the
- * finalize's status: E_ENERGY, E_NONFINITE, E_NOCONV or E_RANK leave the previous
- * projections active. B may be 0 when x and gy are both NULL. */
+ * the sums. A finalize needs samples on both sides (else E_STATE).
+ *   INSTANT_FINALIZE_SYNC (1): returns once done, with the finalize's status:
+ *     E_ENERGY, E_NONFINITE, E_NOCONV or E_RANK leave the previous projections active.
+ *   INSTANT_FINALIZE_ASYNC (2): queues the same work on `stream` and returns E_OK at
+ *     once; the host does not wait. The outcome is applied by the first
+ *     instant_compress_fwd after the device has finished it (that call then uses the new
+ *     projections; instant_backward never switches them, so a compress / backward pair
+ *     uses one set), or by instant_query, instant_get_projections,
+ *     instant_set_projections, the next finalize, which wait for it. Until then the
+ *     previous projections stay active and the status is read by instant_query. The
+ *     decomposition runs on the handle's workspace alongside calls on other streams;
+ *     it rewrites the inactive projection buffer, so it must be ordered after earlier
+ *     calls that read that buffer while it was active (as for a synchronous finalize).
+ * The finalize's outcome reaches the host through a small pinned host buffer that the
+ * handle allocates at creation. B may be 0 when x and gy are both NULL. */
 instant_status instant_calibrate(instant_layer* h, const void* x, const void* gy, int32_t B,
                                  int32_t finalize, void* stream);
 

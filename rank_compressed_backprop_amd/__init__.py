@@ -37,6 +37,7 @@ INSTANT_E_ENERGY, INSTANT_E_NONFINITE, INSTANT_E_NOCONV, INSTANT_E_HIP = 5, 6, 7
 INSTANT_FP32, INSTANT_BF16 = 0, 1
 INSTANT_COMP_PAPER, INSTANT_COMP_NONE, INSTANT_COMP_RATIO = 0, 1, 2
 INSTANT_SOLVER_JACOBI, INSTANT_SOLVER_SUBSPACE = 0, 1
+INSTANT_FINALIZE_NONE, INSTANT_FINALIZE_SYNC, INSTANT_FINALIZE_ASYNC = 0, 1, 2
 
 
 class instant_config(ctypes.Structure):
@@ -125,8 +126,10 @@ def instant_destroy(h) -> int:
     return _lib.instant_destroy(h)
 
 
-def instant_calibrate(h, x, gy, B: int, finalize: bool, stream=None) -> int:
-    return _lib.instant_calibrate(h, _ptr(x), _ptr(gy), int(B), int(bool(finalize)), _stream(stream))
+def instant_calibrate(h, x, gy, B: int, finalize, stream=None) -> int:
+    """finalize: False / 0 (none), True / 1 (synchronous), "async" / 2 (asynchronous)."""
+    mode = INSTANT_FINALIZE_ASYNC if finalize == "async" else int(finalize)
+    return _lib.instant_calibrate(h, _ptr(x), _ptr(gy), int(B), mode, _stream(stream))
 
 
 def instant_compress_fwd(h, x, B: int, xhat, stream=None) -> int:

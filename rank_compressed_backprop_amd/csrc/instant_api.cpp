@@ -129,6 +129,13 @@ struct instant_layer {
   int ncu;  // compute units of the device the handle was created on
   instant_info info;
   instant_status last;
+  // outcome of the last finalize: copied by the device into pinned host memory; with an
+  // asynchronous finalize it is settled once `done` has passed (pending until then)
+  int* hflags;
+  hipEvent_t done;
+  bool pending;
+  int pend_t, pend_m;
+  int64_t pend_nx, pend_ng;
 
   double* SX() const { return (double*)(ws + lay.SX); }
   double* SG() const { return (double*)(ws + lay.SG); }
@@ -148,6 +155,61 @@ namespace {
 
 inline hipStream_t S(void* stream) { return (hipStream_t)stream; }
 inline instant_status hip_ok(hipError_t e) { return e == hipSuccess ? INSTANT_OK : INSTANT_E_HIP; }
+
+// Applies the outcome of the last finalize from the flags the device copied back: the new
+// projections become active only if both sides succeeded.
+instant_status settle(instant_layer* h) {
+  const int* flags = h->hflags;
+  const int* ix = flags + EIGF_INFO;
+  const int* ig = flags + EIGF_INFO + INFO_WORDS;
+  instant_status status = (instant_status)(ix[0] != 0 ? ix[0] : ig[0]);
+  if (flags[EIGF_ABORT]) status = INSTANT_E_HIP;  // a bounded wait of the eigensolver gave up
+
+  instant_info& I = h->info;
+  I.kx = ix[1];
+  I.ky = ig[1];
+  I.sweeps_x = flags[EIGF_SWEEPS];
+  I.sweeps_g = flags[EIGF_SWEEPS + 1];
+  I.status = status;
+  float c;
+  std::memcpy(&c, &ix[3], 4);
+  I.cP = c;
+  std::memcpy(&c, &ig[3], 4);
+  I.cQ = c;
+  std::memcpy(&I.kept_x, &ix[4], 8);
+  std::memcpy(&I.kept_g, &ig[4], 8);
+  I.n_samples_x = h->pend_nx;
+  I.n_samples_g = h->pend_ng;
+  if (status == INSTANT_OK) {
+    h->active = h->pend_t;
+    h->Rx = ix[2];
+    h->Ry = ig[2];
+    I.Rx = h->Rx;
+    I.Ry = h->Ry;
+    I.generation += 1;
+  }
+  h->last = status;
+  // a failed decomposition may leave the accumulated rotation unusable: restart cold (a
+  // subspace basis that has not converged yet is still the best start for the next one)
+  h->warm = (status == INSTANT_OK || status == INSTANT_E_RANK) ||
+            (h->pend_m > 0 && status == INSTANT_E_NOCONV);
+  return status;
+}
+
+// Settles an asynchronous finalize whose work has completed (or, with wait, once it has).
+void apply_pending(instant_layer* h, bool wait) {
+  if (!h->pending) return;
+  hipError_t e = wait ? hipEventSynchronize(h->done) : hipEventQuery(h->done);
+  if (e == hipErrorNotReady) return;
+  h->pending = false;
+  if (e != hipSuccess) {
+    h->warm = false;
+    h->last = INSTANT_E_HIP;
+    h->info.status = INSTANT_E_HIP;
+    return;
+  }
+  settle(h);
+}
 
 // Both statistics of a batch (either input may be NULL) in one SYRK launch.
 instant_status accumulate(instant_layer* h, const void* x, const void* gy, int B, hipStream_t st) {
@@ -182,10 +244,27 @@ INSTANT_API instant_status instant_create(instant_layer** h, const instant_confi
   L->nx = L->ng = 0;
   std::memset(&L->info, 0, sizeof(L->info));
   L->last = INSTANT_OK;
+  L->pending = false;
+  L->pend_t = L->pend_m = 0;
+  L->pend_nx = L->pend_ng = 0;
+  L->hflags = nullptr;
+  L->done = nullptr;
+  if (hipHostMalloc((void**)&L->hflags, EIG_HOST_FLAGS * sizeof(int), hipHostMallocDefault) != hipSuccess) {
+    delete L;
+    return INSTANT_E_HIP;
+  }
+  std::memset(L->hflags, 0, EIG_HOST_FLAGS * sizeof(int));
+  if (hipEventCreateWithFlags(&L->done, hipEventDisableTiming) != hipSuccess) {
+    (void)hipHostFree(L->hflags);
+    delete L;
+    return INSTANT_E_HIP;
+  }
   int dev = 0;
   L->ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&L->ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || L->ncu < 1) {
+    (void)hipEventDestroy(L->done);
+    (void)hipHostFree(L->hflags);
     delete L;
     return INSTANT_E_HIP;
   }
@@ -194,6 +273,8 @@ INSTANT_API instant_status instant_create(instant_layer** h, const instant_confi
   if (e == hipSuccess) e = launch_zero(L->ws + L->lay.zpad, 256, S(stream));
   if (e == hipSuccess) e = launch_zero(L->SG(), (size_t)cfg->L * cfg->L * sizeof(double), S(stream));
   if (e != hipSuccess) {
+    (void)hipEventDestroy(L->done);
+    (void)hipHostFree(L->hflags);
     delete L;
     return INSTANT_E_HIP;
   }
@@ -203,6 +284,9 @@ INSTANT_API instant_status instant_create(instant_layer** h, const instant_confi
 
 INSTANT_API instant_status instant_destroy(instant_layer* h) {
   if (!h) return INSTANT_E_ARG;
+  if (h->pending) (void)hipEventSynchronize(h->done);  // the device may still write hflags
+  (void)hipEventDestroy(h->done);
+  (void)hipHostFree(h->hflags);
   delete h;
   return INSTANT_OK;
 }
@@ -213,6 +297,7 @@ INSTANT_API instant_status instant_calibrate(instant_layer* h, const void* x, co
   if (B < 0 || B > h->cfg.B_max) return (B < 0) ? INSTANT_E_ARG : INSTANT_E_SHAPE;
   if ((x || gy) && B < 1) return INSTANT_E_ARG;
   if (!x && !gy && !finalize) return INSTANT_E_ARG;
+  if (finalize != 0 && finalize != INSTANT_FINALIZE_SYNC && finalize != INSTANT_FINALIZE_ASYNC) return INSTANT_E_ARG;
   hipStream_t st = S(stream);
   if (finalize) {
     const int64_t nx = h->nx + (x ? B : 0), ng = h->ng + (gy ? B : 0);
@@ -226,6 +311,7 @@ INSTANT_API instant_status instant_calibrate(instant_layer* h, const void* x, co
   }
   if (!finalize) return INSTANT_OK;
 
+  apply_pending(h, true);  // the previous finalize's outcome decides which buffer is free
   const int t = (h->active == 0) ? 1 : 0;
   EigOut out;
   out.eps = h->cfg.eps;
@@ -254,57 +340,38 @@ INSTANT_API instant_status instant_calibrate(instant_layer* h, const void* x, co
                            hh->info_dev() + INFO_WORDS + 2, hh->cfg.L, hh->lay.ldL, hh->cfg.R_max, hh->PQ(tl.t),
                            hh->Qt(tl.t), LD_QT, st);
   };
-  int flags[EIG_HOST_FLAGS];
   const int m = h->cfg.solver == INSTANT_SOLVER_SUBSPACE ? eig_subspace_width(h->cfg.L, h->cfg.R_max) : 0;
+  const bool async = finalize == INSTANT_FINALIZE_ASYNC;
   hipError_t e = m > 0 ? run_eig_subspace(h->SX(), h->SG(), 1.0 / (double)h->nx, 1.0 / (double)h->ng, h->cfg.L, m,
                                           h->cfg.sub_iters, h->cfg.max_sweeps, h->warm, h->ws + h->lay.eig, out,
-                                          flags, st)
+                                          h->hflags, st, !async)
                        : run_eig(h->SX(), h->SG(), 1.0 / (double)h->nx, 1.0 / (double)h->ng, h->cfg.L,
-                                 h->cfg.max_sweeps, h->warm, h->ws + h->lay.eig, out, flags, st);
+                                 h->cfg.max_sweeps, h->warm, h->ws + h->lay.eig, out, h->hflags, st, !async);
+  if (e == hipSuccess && async) e = hipEventRecord(h->done, st);
   if (e != hipSuccess) {
     h->warm = false;
+    h->nx = h->ng = 0;
     return INSTANT_E_HIP;
   }
-  const int* ix = flags + EIGF_INFO;
-  const int* ig = flags + EIGF_INFO + INFO_WORDS;
-  instant_status status = (instant_status)(ix[0] != 0 ? ix[0] : ig[0]);
-
-  instant_info& I = h->info;
-  I.kx = ix[1];
-  I.ky = ig[1];
-  I.sweeps_x = flags[EIGF_SWEEPS];
-  I.sweeps_g = flags[EIGF_SWEEPS + 1];
-  I.status = status;
-  float c;
-  std::memcpy(&c, &ix[3], 4);
-  I.cP = c;
-  std::memcpy(&c, &ig[3], 4);
-  I.cQ = c;
-  std::memcpy(&I.kept_x, &ix[4], 8);
-  std::memcpy(&I.kept_g, &ig[4], 8);
-  I.n_samples_x = h->nx;
-  I.n_samples_g = h->ng;
-  if (status == INSTANT_OK) {
-    h->active = t;
-    h->Rx = ix[2];
-    h->Ry = ig[2];
-    I.Rx = h->Rx;
-    I.Ry = h->Ry;
-    I.generation += 1;
+  h->pend_t = t;
+  h->pend_m = m;
+  h->pend_nx = h->nx;
+  h->pend_ng = h->ng;
+  h->nx = h->ng = 0;  // the window is consumed whatever the outcome
+  if (async) {
+    h->pending = true;
+    return INSTANT_OK;
   }
-  h->last = status;
-  // a failed decomposition may leave the accumulated rotation unusable: restart cold (a
-  // subspace basis that has not converged yet is still the best start for the next one)
-  h->warm = (status == INSTANT_OK || status == INSTANT_E_RANK) ||
-            (m > 0 && status == INSTANT_E_NOCONV);
-  h->nx = h->ng = 0;
-  return status;
+  return settle(h);
 }
 
 INSTANT_API instant_status instant_compress_fwd(instant_layer* h, const void* x, int32_t B, void* xhat,
                                                 void* stream) {
   if (!h || !x || !xhat || B < 1) return INSTANT_E_ARG;
   if (B > h->cfg.B_max) return INSTANT_E_SHAPE;
+  // a finished asynchronous finalize takes effect here, at a forward (waited for only when
+  // no projections are active yet), so a compress / backward pair uses one set
+  apply_pending(h, h->active < 0);
   if (h->active < 0) return INSTANT_E_STATE;
   const int a = h->active;
   return hip_ok(launch_proj(h->bf16, h->PQ(a), h->lay.ldL, h->Rx, h->Rx, x, B, h->cfg.L, h->cfg.Cx, xhat, nullptr,
@@ -341,6 +408,7 @@ INSTANT_API instant_status instant_backward(instant_layer* h, const void* xhat, 
 
 INSTANT_API instant_status instant_query(instant_layer* h, instant_info* out) {
   if (!h || !out) return INSTANT_E_ARG;
+  apply_pending(h, true);
   *out = h->info;
   return h->last;
 }
@@ -349,6 +417,7 @@ INSTANT_API instant_status instant_set_projections(instant_layer* h, const float
                                                    int32_t Ry, void* stream) {
   if (!h || !P || !Q) return INSTANT_E_ARG;
   if (Rx < 1 || Ry < 1 || Rx > h->cfg.R_max || Ry > h->cfg.R_max) return INSTANT_E_SHAPE;
+  apply_pending(h, true);
   hipStream_t st = S(stream);
   const int t = (h->active == 0) ? 1 : 0;
   const size_t L = h->cfg.L;
@@ -373,6 +442,7 @@ INSTANT_API instant_status instant_set_projections(instant_layer* h, const float
 INSTANT_API instant_status instant_get_projections(instant_layer* h, float* P, float* Q, float* sigma_x,
                                                    float* sigma_g, void* stream) {
   if (!h) return INSTANT_E_ARG;
+  apply_pending(h, true);
   if ((P || Q) && h->active < 0) return INSTANT_E_STATE;
   hipStream_t st = S(stream);
   const size_t L = h->cfg.L;

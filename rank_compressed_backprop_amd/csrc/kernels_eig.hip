@@ -889,7 +889,8 @@ __global__ __launch_bounds__(1024) void truncate_build_kernel(TruncArgs a, int l
 // ---------------------------------------------------------------------------- driver
 
 hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv_ng, int L, int max_sweeps,
-                   bool warm, void* work, const EigOut& out, int host_flags[EIG_HOST_FLAGS], hipStream_t st) {
+                   bool warm, void* work, const EigOut& out, int host_flags[EIG_HOST_FLAGS], hipStream_t st,
+                   bool wait) {
   if (L > JAC_MAX_LDW) return hipErrorInvalidValue;
   const EigLayout e = eig_layout(L);
   const EigBufs b = eig_bufs(work, e);
@@ -984,6 +985,7 @@ hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv
   if (out.before_readback && (err = out.before_readback(out.ctx, st)) != hipSuccess) return err;
   if ((err = hipMemcpyAsync(host_flags, flags, EIG_HOST_FLAGS * sizeof(int), hipMemcpyDeviceToHost, st)) != hipSuccess)
     return err;
+  if (!wait) return hipSuccess;  // the caller settles the outcome once the stream has passed here
   if ((err = hipStreamSynchronize(st)) != hipSuccess) return err;
   if (host_flags[F_ABORT]) return hipErrorLaunchTimeOut;  // a bounded wait gave up
   return hipSuccess;
@@ -1093,7 +1095,7 @@ __global__ __launch_bounds__(256) void sub_normalize_kernel(EigSides a, float* r
 
 hipError_t run_eig_subspace(const double* SX, const double* SG, double inv_nx, double inv_ng, int L, int m,
                             int iters, int max_sweeps, bool warm, void* work, const EigOut& out,
-                            int host_flags[EIG_HOST_FLAGS], hipStream_t st) {
+                            int host_flags[EIG_HOST_FLAGS], hipStream_t st, bool wait) {
   if (L > JAC_MAX_LDW || m < 16 || m % 16 || m >= L || iters < 1) return hipErrorInvalidValue;
   const EigLayout e = eig_layout(L);
   const EigBufs b = eig_bufs(work, e);
@@ -1194,6 +1196,7 @@ hipError_t run_eig_subspace(const double* SX, const double* SG, double inv_nx, d
   if (out.before_readback && (err = out.before_readback(out.ctx, st)) != hipSuccess) return err;
   if ((err = hipMemcpyAsync(host_flags, flags, EIG_HOST_FLAGS * sizeof(int), hipMemcpyDeviceToHost, st)) != hipSuccess)
     return err;
+  if (!wait) return hipSuccess;
   if ((err = hipStreamSynchronize(st)) != hipSuccess) return err;
   if (host_flags[F_ABORT]) return hipErrorLaunchTimeOut;
   return hipSuccess;

@@ -55,8 +55,11 @@ int syrk_tiles(int L);
 // projections P32 [Rx][L] / Q32 [Ry][L], the descending spectra and the per-side
 // device info blocks (int32 slots: status, k, R, c bits, kept (f64), kept_k (f64)).
 // warm: start from the rotation accumulated by the previous call (kept in `work`).
-// Synchronous (one stream synchronisation at the end). host_flags receives the
-// first EIG_HOST_FLAGS int32 slots of the flags block (see kernels_eig.hip).
+// host_flags receives the first EIG_HOST_FLAGS int32 slots of the flags block (see
+// kernels_eig.hip) through a copy queued on `st`. wait: synchronise the stream at the end
+// and turn an aborted wait into hipErrorLaunchTimeOut; otherwise return once everything is
+// queued (host_flags must then be pinned memory, valid after the stream passes the copy,
+// and slot EIGF_ABORT tells whether a bounded wait gave up).
 struct EigOut {
   float eps;
   int p, comp, R_max;
@@ -73,7 +76,7 @@ struct EigOut {
 };
 constexpr int INFO_WORDS = 8;
 constexpr int EIG_HOST_FLAGS = 40;
-constexpr int EIGF_SWEEPS = 6, EIGF_CONV = 8, EIGF_BAD = 10, EIGF_NALIVE = 18, EIGF_INFO = 24;
+constexpr int EIGF_SWEEPS = 6, EIGF_CONV = 8, EIGF_BAD = 10, EIGF_ABORT = 17, EIGF_NALIVE = 18, EIGF_INFO = 24;
 size_t eig_workspace_bytes(int L);
 int eig_max_L();
 // Subspace width for the top-R solver (0 when it would span the whole space).
@@ -83,9 +86,10 @@ int eig_subspace_width(int L, int R_max);
 // whose Ritz residual exceeds its tolerance, and (status 4) thresholds beyond m directions.
 hipError_t run_eig_subspace(const double* SX, const double* SG, double inv_nx, double inv_ng, int L, int m,
                             int iters, int max_sweeps, bool warm, void* work, const EigOut& out,
-                            int host_flags[EIG_HOST_FLAGS], hipStream_t st);
+                            int host_flags[EIG_HOST_FLAGS], hipStream_t st, bool wait);
 hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv_ng, int L, int max_sweeps,
-                   bool warm, void* work, const EigOut& out, int host_flags[EIG_HOST_FLAGS], hipStream_t st);
+                   bool warm, void* work, const EigOut& out, int host_flags[EIG_HOST_FLAGS], hipStream_t st,
+                   bool wait);
 
 // I/O-dtype copies of the active projections: PQ [2*R_max][ldL] (rows [0,Rx) = P,
 // [Rx,Rx+Ry) = Q, zero elsewhere) and Qt [L][ldQt] (zero beyond Ry).

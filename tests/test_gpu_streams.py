@@ -74,3 +74,65 @@ def test_statistics_on_a_second_stream_match_serial():
     assert torch.equal(ref[1], got[1]) and torch.equal(ref[2], got[2])
     assert (ref[3].Rx, ref[3].Ry, ref[3].kx, ref[3].ky) == (got[3].Rx, got[3].Ry, got[3].kx, got[3].ky)
     print(f"[streams] identical: Rx {got[3].Rx} Ry {got[3].Ry}", flush=True)
+
+
+def test_async_finalize_matches_sync_and_switches_at_a_forward():
+    """An asynchronous finalize (queued on a side stream, no host wait) publishes the same
+    projections bit for bit as a synchronous one; they take effect at the first forward
+    compression after the device has finished the finalize, and instant_query waits for it."""
+    import rank_compressed_backprop_amd as rcb
+    from gpu_util import empty, to_dev
+    wl = W.get_workload("bert_attn")
+    ly = wl.layer(0)
+    B, L, Cx, Cy = 8, wl.L, ly.Cx, ly.Cy
+    batches = []
+    for t in range(8):
+        d = W.make_layer_batch(wl, 0, 400 + t)
+        batches.append((to_dev(d["x"][:B], "bf16"), to_dev(d["gy"][:B], "bf16")))
+    cfg = dict(R_max=64, p=2, dtype="bf16")
+    ref = rcb.InstantLayer(rcb.make_config(L, Cx, Cy, B, **cfg))
+    lay = rcb.InstantLayer(rcb.make_config(L, Cx, Cy, B, **cfg))
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+
+    def window(ws):
+        for x, g in ws[:-1]:
+            assert ref.calibrate(x, g, B) == 0
+            assert lay.calibrate(x, g, B, stream=side) == 0
+        x, g = ws[-1]
+        s = ref.calibrate(x, g, B, finalize=True)
+        assert s == rcb.INSTANT_OK, rcb.instant_status_str(s)
+        side.wait_stream(main)
+        assert lay.calibrate(x, g, B, finalize="async", stream=side) == rcb.INSTANT_OK
+
+    def proj(l, info):
+        P = torch.empty((info.Rx, L), device="cuda")
+        Q = torch.empty((info.Ry, L), device="cuda")
+        l.get_projections(P, Q)
+        torch.cuda.synchronize()
+        return P, Q
+
+    # first window: query waits for the asynchronous outcome
+    window(batches[:4])
+    side.wait_stream(main)
+    s, info = lay.query()
+    _, info_r = ref.query()
+    assert s == rcb.INSTANT_OK and info.generation == 1
+    assert (info.kx, info.Rx, info.ky, info.Ry) == (info_r.kx, info_r.Rx, info_r.ky, info_r.Ry)
+    for a, b in zip(proj(lay, info), proj(ref, info_r)):
+        assert torch.equal(a, b)
+
+    # second window: once the device has finished, the next forward uses the new projections
+    window(batches[4:])
+    torch.cuda.synchronize()
+    x = batches[0][0]
+    xh_l, xh_r = empty((B, 64, Cx), "bf16"), empty((B, 64, Cx), "bf16")
+    lay.compress_fwd(x, B, xh_l)  # raises on an error status
+    ref.compress_fwd(x, B, xh_r)
+    torch.cuda.synchronize()
+    _, info = lay.query()
+    _, info_r = ref.query()
+    assert info.generation == 2 and info_r.generation == 2
+    n = B * info.Rx * Cx
+    assert torch.equal(xh_l.view(-1)[:n].view(torch.int16), xh_r.view(-1)[:n].view(torch.int16))
+    print(f"[streams] asynchronous finalize identical: Rx {info.Rx} Ry {info.Ry}", flush=True)
