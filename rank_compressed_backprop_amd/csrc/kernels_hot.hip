@@ -118,7 +118,7 @@ __global__ __launch_bounds__(NW * WAVE) void proj_kernel(const T* __restrict__ A
 // Block (bx, by, bz) of the grid described above, computed by NW waves numbered `wave` =
 // 0 .. NW-1 (all waves of the workgroup call it the same number of times: it holds block
 // barriers); `red` is NW * 8 KB of LDS.
-template <class T, bool A_TRANS, int MT, int NW, int U>
+template <class T, bool A_TRANS, int MT, int NW, int U, bool NT = false>
 __device__ __forceinline__ void gemm_block(const T* __restrict__ A, int lda, size_t strideA,
                                            const T* __restrict__ Bm, int ldb, size_t strideB, T* __restrict__ Cm,
                                            int ldc, size_t strideC, int M, int N, int K, int bx, int by, int bz,
@@ -184,7 +184,10 @@ __device__ __forceinline__ void gemm_block(const T* __restrict__ A, int lda, siz
     return A_TRANS ? m0 + 4 * r + t : m0 + 16 * t + r;
   };
   auto store = [&](int m, const float o[8]) {
-    if (m < M && col_ok) store_row<T, 8>(Cm + (size_t)m * ldc + col, o);
+    if (m < M && col_ok) {
+      if constexpr (NT) store_row_nt<T, 8>(Cm + (size_t)m * ldc + col, o);
+      else store_row<T, 8>(Cm + (size_t)m * ldc + col, o);
+    }
   };
 
   if constexpr (NW == 1) {
@@ -221,14 +224,15 @@ __device__ __forceinline__ void gemm_block(const T* __restrict__ A, int lda, siz
   }
 }
 
-template <class T, bool A_TRANS, int MT, int NW, int U>
-__global__ __launch_bounds__(NW * WAVE) void gemm_kernel(const T* __restrict__ A, int lda, size_t strideA,
-                                                         const T* __restrict__ Bm, int ldb, size_t strideB,
-                                                         T* __restrict__ Cm, int ldc, size_t strideC,
-                                                         int M, int N, int K) {
+// WPE: the fewest waves each SIMD must be able to hold (caps the registers a wave may use);
+// NT: non-temporal stores, for an output that neither this launch nor the next one reads.
+template <class T, bool A_TRANS, int MT, int NW, int U, int WPE = 1, bool NT = false>
+__global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(WPE, 8))) void gemm_kernel(
+    const T* __restrict__ A, int lda, size_t strideA, const T* __restrict__ Bm, int ldb, size_t strideB,
+    T* __restrict__ Cm, int ldc, size_t strideC, int M, int N, int K) {
   __shared__ float red[NW][8][4][WAVE];
-  gemm_block<T, A_TRANS, MT, NW, U>(A, lda, strideA, Bm, ldb, strideB, Cm, ldc, strideC, M, N, K, blockIdx.x,
-                                    blockIdx.y, blockIdx.z, threadIdx.x / WAVE, red);
+  gemm_block<T, A_TRANS, MT, NW, U, NT>(A, lda, strideA, Bm, ldb, strideB, Cm, ldc, strideC, M, N, K, blockIdx.x,
+                                        blockIdx.y, blockIdx.z, threadIdx.x / WAVE, red);
 }
 
 // ----------------------------------------------------------------------------- expand
@@ -523,12 +527,12 @@ hipError_t launch_proj(bool bf16_io, const void* A, int ldA, int M, int M0, cons
                  : proj_t<float>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
 }
 
-template <class T, bool AT, int MT, int NW, int U>
+template <class T, bool AT, int MT, int NW, int U, int WPE = 1, bool NT = false>
 static hipError_t gemm_cfg(const void* A, int lda, size_t sA, const void* Bm, int ldb, size_t sB, void* Cm, int ldc,
                            size_t sC, int batch, int M, int N, int K, hipStream_t st) {
   constexpr int ROWS = AT ? 64 : 16 * MT;
   dim3 grid((N + 127) / 128, (M + ROWS - 1) / ROWS, batch);
-  hipLaunchKernelGGL((gemm_kernel<T, AT, MT, NW, U>), grid, dim3(NW * WAVE), 0, st, (const T*)A, lda, sA,
+  hipLaunchKernelGGL((gemm_kernel<T, AT, MT, NW, U, WPE, NT>), grid, dim3(NW * WAVE), 0, st, (const T*)A, lda, sA,
                      (const T*)Bm, ldb, sB, (T*)Cm, ldc, sC, M, N, K);
   return hipGetLastError();
 }
@@ -542,12 +546,15 @@ static hipError_t gemm_t(const void* A, int lda, size_t sA, const void* Bm, int 
   if constexpr (AT) {
     if constexpr (BF) {
       // (bf16, measured on gfx950) Many 64x128 tiles (g_w of an LLM MLP: 5504 at 11008 x 4096,
-      // K = 272): one wave per tile with the whole K in three rounds of loads, 76.8 us against
-      // 122 us for two waves splitting K. Few tiles (BERT FFN, 288 at K = 448; EfficientFormer,
-      // 112 at K = 3712): four waves split K, 10.8-11.4 us against 12.0-12.5 us with two, and
-      // 34 us against 57 us at the long K with two steps in flight per wave.
+      // K = 272): one wave per tile, one step of loads in flight, registers capped so that two
+      // waves share a SIMD (one hides the other's loads), non-temporal stores: 44 us, against
+      // 73-77 us with one wave per SIMD and three steps in flight, and 122 us for two waves
+      // splitting K. Few tiles (BERT FFN, 288 at K = 448; EfficientFormer, 112 at K = 3712):
+      // four waves split K, 10.8-11.4 us against 12.0-12.5 us with two, and 34 us against
+      // 57 us at the long K with two steps in flight per wave.
       const long tiles = strips * ((M + 63) / 64);
-      if (tiles >= 2048) return gemm_cfg<T, true, 4, 1, 3>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
+      if (tiles >= 2048)
+        return gemm_cfg<T, true, 4, 1, 1, 2, true>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
       if (nsteps <= 16) return gemm_cfg<T, true, 4, 4, 1>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
       return gemm_cfg<T, true, 4, 4, 2>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
     }
