@@ -1,8 +1,7 @@
 // Per-step kernels of the INSTANT low-rank backward (notes "INSTANT: Compressing
 // Gradients and Activations for Resource-Efficient Training", sections 整体框架 and
-// 关键设计 3):
-//   proj    x_hat_b = P x_b (forward compression) and, with the stacked [P; Q],
-//           P gy_b and Q gy_b from a single read of gy
+// 关键设计 3); the projection (forward compression and the stacked [P; Q] gy) is in
+// kernels_proj.hip:
 //   gemm    g_w = sum_b (P gy_b)^T x_hat_b   (contraction over K = B*Rx)
 //           g_hat_x = (Q gy) w               (contraction over K = Cy)
 //   expand  g_x_b = Q^T g_hat_x_b            (contraction over K = Ry)
@@ -13,99 +12,6 @@
 #include "launch.hpp"
 
 namespace instant {
-
-// ----------------------------------------------------------------------------- proj
-// Out[b][m][c] = sum_{l < L} A[m][l] X[b][l][c] for m < M, c < C.
-// A is [>= M rows][ldA] with zero columns from L up to ldA (ldA a multiple of KSTEP).
-// Rows m < M0 go to out0 [B][M0][C]; rows M0 <= m < M go to out1 [B][M - M0][C].
-// Grid: (ceil(C / (16 * SW)), B). A lane owns SW adjacent columns; the NW waves of a
-// block take every NW-th k-step of the same column strip and issue the loads of U
-// steps before any product; the partial tiles are summed through LDS in wave order.
-template <class T, int MT, int NW, int U, int SW>
-__global__ __launch_bounds__(NW * WAVE) void proj_kernel(const T* __restrict__ A, int ldA, int M, int M0,
-                                                         const T* __restrict__ X, int L, int C,
-                                                         T* __restrict__ out0, T* __restrict__ out1) {
-  typedef MM<T> mm;
-  typedef typename mm::frag frag;
-  const int lane = threadIdx.x & (WAVE - 1);
-  const int wave = threadIdx.x / WAVE;
-  const int b = blockIdx.y;
-  const int col = blockIdx.x * (16 * SW) + SW * (lane & 15);
-  const bool col_ok = col < C;
-  const T* __restrict__ Xb = X + (size_t)b * L * C;
-  const int arow = lane & 15;
-  const int kl = mm::G * (lane >> 4);
-
-  f32x4 acc[MT][SW];
-#pragma unroll
-  for (int t = 0; t < MT; ++t)
-#pragma unroll
-    for (int j = 0; j < SW; ++j) acc[t][j] = zero4();
-
-  const int nsteps = (L + mm::KSTEP - 1) / mm::KSTEP;
-  for (int s0 = wave; s0 < nsteps; s0 += NW * U) {
-    frag bf[U][SW];
-    frag af[U][MT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = s0 + u * NW;
-      const int k0 = s * mm::KSTEP + kl;
-      load_strip_T<T, SW>(Xb, C, k0, L, col, col_ok, bf[u]);
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const int m = 16 * t + arow;
-        af[u][t] = load_frag<T>(A + (size_t)m * ldA + k0, m < M && s < nsteps);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-#pragma unroll
-        for (int j = 0; j < SW; ++j) acc[t][j] = mm::mma(af[u][t], bf[u][j], acc[t][j]);
-  }
-
-  const int Mb = M - M0;
-  auto store = [&](int m, const float v[SW]) {
-    if (m >= M || !col_ok) return;
-    T* dst = (m < M0) ? out0 + ((size_t)b * M0 + m) * C + col : out1 + ((size_t)b * Mb + (m - M0)) * C + col;
-    store_row<T, SW>(dst, v);
-  };
-
-  if constexpr (NW == 1) {
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float o[SW];
-#pragma unroll
-        for (int j = 0; j < SW; ++j) o[j] = acc[t][j][v];
-        store(16 * t + 4 * (lane >> 4) + v, o);
-      }
-  } else {
-    __shared__ float red[NW][SW][4][WAVE];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-#pragma unroll
-      for (int j = 0; j < SW; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) red[wave][j][v][lane] = acc[t][j][v];
-      __syncthreads();
-      for (int v = wave; v < 4; v += NW) {
-        float o[SW];
-#pragma unroll
-        for (int j = 0; j < SW; ++j) {
-          float sum = red[0][j][v][lane];
-#pragma unroll
-          for (int w = 1; w < NW; ++w) sum += red[w][j][v][lane];
-          o[j] = sum;
-        }
-        store(16 * t + 4 * (lane >> 4) + v, o);
-      }
-      __syncthreads();
-    }
-  }
-}
 
 // ----------------------------------------------------------------------------- gemm
 // Cm[m][n] = sum_{k < K} A(m, k) B[k][n], written in T to Cm [M][ldc] (batch-strided).
@@ -471,61 +377,6 @@ __global__ __launch_bounds__(NW * WAVE) void bwd_tail_kernel(const T* __restrict
 }
 
 // ----------------------------------------------------------------------------- launchers
-
-template <class T, int MT, int NW, int SW>
-static hipError_t proj_cfg(const void* A, int ldA, int M, int M0, const void* X, int B, int L, int C, void* out0,
-                           void* out1, hipStream_t st) {
-  // loads in flight vs registers; with eight waves a strip is already split finely
-  constexpr int U = NW >= 8 ? (MT <= 2 ? 2 : 1) : (MT <= 2 ? 4 : (MT <= 5 ? 2 : 1));
-  dim3 grid((C + 16 * SW - 1) / (16 * SW), B);
-  hipLaunchKernelGGL((proj_kernel<T, MT, NW, U, SW>), grid, dim3(NW * WAVE), 0, st, (const T*)A, ldA, M, M0,
-                     (const T*)X, L, C, (T*)out0, (T*)out1);
-  return hipGetLastError();
-}
-
-template <class T, int MT>
-static hipError_t proj_mt(const void* A, int ldA, int M, int M0, const void* X, int B, int L, int C, void* out0,
-                          void* out1, hipStream_t st) {
-  const int nsteps = (L + MM<T>::KSTEP - 1) / MM<T>::KSTEP;
-  // eight waves per strip keep the most loads in flight per compute unit (measured on
-  // gfx950 at B=32, L=512, C=768); narrower strips when 128-column strips would leave
-  // compute units idle and the token axis is short
-  const bool narrow = (long)((C + 127) / 128) * B < 256 && C > 64 && nsteps < 8;
-  // (512-thread blocks leave 256 registers per lane: only the narrow stacks fit)
-  if constexpr (MT <= 2) {
-    if (nsteps >= 8) return proj_cfg<T, MT, 8, 8>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
-  }
-  if (nsteps >= 4)
-    return narrow ? proj_cfg<T, MT, 4, 4>(A, ldA, M, M0, X, B, L, C, out0, out1, st)
-                  : proj_cfg<T, MT, 4, 8>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
-  if (nsteps >= 2)
-    return narrow ? proj_cfg<T, MT, 2, 4>(A, ldA, M, M0, X, B, L, C, out0, out1, st)
-                  : proj_cfg<T, MT, 2, 8>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
-  return narrow ? proj_cfg<T, MT, 1, 4>(A, ldA, M, M0, X, B, L, C, out0, out1, st)
-                : proj_cfg<T, MT, 1, 8>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
-}
-
-template <class T>
-static hipError_t proj_t(const void* A, int ldA, int M, int M0, const void* X, int B, int L, int C,
-                         void* out0, void* out1, hipStream_t st) {
-  switch ((M + 15) / 16) {
-    case 1: return proj_mt<T, 1>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
-    case 2: return proj_mt<T, 2>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
-    case 3: return proj_mt<T, 3>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
-    case 4: return proj_mt<T, 4>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
-    case 5: return proj_mt<T, 5>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
-    case 6: return proj_mt<T, 6>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
-    case 7: return proj_mt<T, 7>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
-    case 8: return proj_mt<T, 8>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t launch_proj(bool bf16_io, const void* A, int ldA, int M, int M0, const void* X, int B, int L, int C,
-                       void* out0, void* out1, hipStream_t st) {
-  return bf16_io ? proj_t<bf16>(A, ldA, M, M0, X, B, L, C, out0, out1, st)
-                 : proj_t<float>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
-}
 
 template <class T, bool AT, int MT, int NW, int U, int WPE = 1, bool NT = false>
 static hipError_t gemm_cfg(const void* A, int lda, size_t sA, const void* Bm, int ldb, size_t sB, void* Cm, int ldc,
