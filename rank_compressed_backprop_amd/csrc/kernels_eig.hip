@@ -1009,7 +1009,8 @@ int eig_max_L() { return JAC_MAX_LDW; }
 // finalize starts the next; the first starts from pseudo-random columns.
 
 constexpr float SUB_RES_TOL = 3e-5f;  // kept Ritz residuals, relative to sigma_0
-constexpr double SUB_NOISE_REL = 1e-30;  // only columns without energy stay out of the rotations
+constexpr int SUB_MAX_DEAD = 32;  // near-null basis columns completed per side and step (the rest are zeroed)
+constexpr int SUB_CT = 1024;      // threads of the completion kernel (latency-bound: as many waves as fit)
 
 int eig_subspace_width(int L, int R_max) {
   const int m = (R_max + 16 + 15) / 16 * 16;  // 16 more directions than the largest rank, whole blocks
@@ -1071,18 +1072,21 @@ __global__ __launch_bounds__(256) void sub_reset_kernel(EigSides a, int* __restr
 }
 
 // After each Jacobi launch: the new basis u_c = W[:, c] / sigma_c and the Ritz residual
-// sigma_c ||u_c - (V J)_c||.
-__global__ __launch_bounds__(256) void sub_normalize_kernel(EigSides a, float* res0, float* res1, int ldw) {
+// sigma_c ||u_c - (V J)_c||. Columns under the noise floor were not rotated: their basis
+// column stays as it was, for sub_complete_kernel to make orthogonal to the new one.
+__global__ __launch_bounds__(256) void sub_normalize_kernel(EigSides a, const double* __restrict__ scale, float* res0,
+                                                            float* res1, int ldw) {
   __shared__ double part[256];
   const int c = blockIdx.x, s = blockIdx.y;
   const float sig = a.nrm[s][c];
+  const bool live = (double)sig * (double)sig > NOISE_REL * scale[s];
   const float inv = sig > 0.0f ? 1.0f / sig : 0.0f;
   double d2 = 0.0;
   for (int r = threadIdx.x; r < ldw; r += 256) {
     const float u = a.W[s][(size_t)c * ldw + r] * inv;
     const double diff = (double)u - a.V[s][(size_t)c * ldw + r];
     d2 += diff * diff;
-    a.V32[s][(size_t)c * ldw + r] = u;
+    if (live) a.V32[s][(size_t)c * ldw + r] = u;
   }
   part[threadIdx.x] = d2;
   __syncthreads();
@@ -1091,6 +1095,111 @@ __global__ __launch_bounds__(256) void sub_normalize_kernel(EigSides a, float* r
     __syncthreads();
   }
   if (threadIdx.x == 0) (s ? res1 : res0)[c] = sig * (float)sqrt(part[0]);
+}
+
+// Completes the basis after a step (one block per side): the columns under the noise floor
+// (whose directions carry no energy, so any orthonormal completion will do) are made
+// orthogonal to the live columns by two passes of classical Gram-Schmidt, then orthonormal
+// among themselves by a Cholesky factorisation of their Gram matrix, all in float64. A
+// column that falls into the span of the others, and every dead column beyond
+// SUB_MAX_DEAD, becomes zero; a zero column stays zero (C 0 = 0) and is never kept.
+__global__ __launch_bounds__(SUB_CT) void sub_complete_kernel(EigSides a, const double* __restrict__ scale, int m,
+                                                            int L, int ldw) {
+  __shared__ int live_c[128], dead_c[128];
+  __shared__ int n_live, n_dead;
+  __shared__ double coef[128 * SUB_MAX_DEAD];
+  __shared__ double gl[SUB_MAX_DEAD * SUB_MAX_DEAD];  // Gram matrix, then its Cholesky factor
+  const int side = blockIdx.x, tid = threadIdx.x;
+  float* __restrict__ V = a.V32[side];
+  if (tid == 0) {
+    int nl = 0, nd = 0;
+    const double floor_g = NOISE_REL * scale[side];
+    for (int c = 0; c < m; ++c) {
+      const double sg = (double)a.nrm[side][c];
+      if (sg * sg > floor_g) live_c[nl++] = c;
+      else dead_c[nd++] = c;
+    }
+    n_live = nl;
+    n_dead = nd;
+  }
+  __syncthreads();
+  const int nl = n_live, nd_all = n_dead;
+  if (nd_all == 0) return;
+  const int nd = nd_all < SUB_MAX_DEAD ? nd_all : SUB_MAX_DEAD;
+  for (int i = nd; i < nd_all; ++i)
+    for (int r = tid; r < L; r += SUB_CT) V[(size_t)dead_c[i] * ldw + r] = 0.0f;
+  const int lane = tid & (WAVE - 1), wave = tid / WAVE;
+  constexpr int NWAVE = SUB_CT / WAVE;
+  // dots of one column x against every dead column at once (float64, fixed order): the
+  // loads of a row are independent, so a wave keeps many of them in flight
+  auto dots_vs_dead = [&](const float* x, double* out) {
+    double acc[SUB_MAX_DEAD];
+#pragma unroll
+    for (int d = 0; d < SUB_MAX_DEAD; ++d) acc[d] = 0.0;
+    for (int r = lane; r < L; r += WAVE) {
+      const double xr = (double)x[r];
+#pragma unroll
+      for (int d = 0; d < SUB_MAX_DEAD; ++d)
+        if (d < nd) acc[d] += xr * (double)V[(size_t)dead_c[d] * ldw + r];
+    }
+#pragma unroll
+    for (int d = 0; d < SUB_MAX_DEAD; ++d) {
+      if (d >= nd) break;
+      double v = acc[d];
+      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+      if (lane == 0) out[d] = v;
+    }
+  };
+  // two passes: v_d -= sum_j (u_j . v_d) u_j over the live columns
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int j = wave; j < nl; j += NWAVE) dots_vs_dead(V + (size_t)live_c[j] * ldw, coef + j * SUB_MAX_DEAD);
+    __syncthreads();
+    for (int r = tid; r < L; r += SUB_CT) {
+      double v[SUB_MAX_DEAD];
+#pragma unroll
+      for (int d = 0; d < SUB_MAX_DEAD; ++d) v[d] = d < nd ? (double)V[(size_t)dead_c[d] * ldw + r] : 0.0;
+      for (int j = 0; j < nl; ++j) {
+        const double u = (double)V[(size_t)live_c[j] * ldw + r];
+#pragma unroll
+        for (int d = 0; d < SUB_MAX_DEAD; ++d) v[d] -= coef[j * SUB_MAX_DEAD + d] * u;
+      }
+#pragma unroll
+      for (int d = 0; d < SUB_MAX_DEAD; ++d)
+        if (d < nd) V[(size_t)dead_c[d] * ldw + r] = (float)v[d];
+    }
+    __syncthreads();
+  }
+  // Gram matrix of the dead columns (row i: dots against every dead column; the lower
+  // triangle is used), then Cholesky on one wave
+  for (int i = wave; i < nd; i += NWAVE) dots_vs_dead(V + (size_t)dead_c[i] * ldw, gl + i * SUB_MAX_DEAD);
+  __syncthreads();
+  if (tid < WAVE) {
+    for (int j = 0; j < nd; ++j) {
+      double sjj = gl[j * SUB_MAX_DEAD + j];
+      for (int k = 0; k < j; ++k) sjj -= gl[j * SUB_MAX_DEAD + k] * gl[j * SUB_MAX_DEAD + k];
+      // the columns had unit norm before the projections: a pivot this small means the column
+      // lies in the span of the others
+      const double ljj = sjj > 1e-8 ? sqrt(sjj) : 0.0;
+      for (int i = j + 1 + tid; i < nd; i += WAVE) {
+        double sij = gl[i * SUB_MAX_DEAD + j];
+        for (int k = 0; k < j; ++k) sij -= gl[i * SUB_MAX_DEAD + k] * gl[j * SUB_MAX_DEAD + k];
+        gl[i * SUB_MAX_DEAD + j] = ljj > 0.0 ? sij / ljj : 0.0;
+      }
+      if (tid == 0) gl[j * SUB_MAX_DEAD + j] = ljj;
+      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+  }
+  __syncthreads();
+  // rows of the dead block times L^-T: forward substitution per row
+  // (a thread solves its own rows: the solved entries it reads back are its own stores)
+  for (int r = tid; r < L; r += SUB_CT) {
+    for (int d = 0; d < nd; ++d) {
+      double v = (double)V[(size_t)dead_c[d] * ldw + r];
+      for (int k = 0; k < d; ++k) v -= gl[d * SUB_MAX_DEAD + k] * (double)V[(size_t)dead_c[k] * ldw + r];
+      const double ldd = gl[d * SUB_MAX_DEAD + d];
+      V[(size_t)dead_c[d] * ldw + r] = ldd > 0.0 ? (float)(v / ldd) : 0.0f;
+    }
+  }
 }
 
 hipError_t run_eig_subspace(const double* SX, const double* SG, double inv_nx, double inv_ng, int L, int m,
@@ -1145,10 +1254,10 @@ hipError_t run_eig_subspace(const double* SX, const double* SG, double inv_nx, d
   ja.ldw = e.ldw;
   ja.nb = nb;
   ja.nc = m;
-  // Every column with energy takes part: the basis must come out orthonormal, and a column
-  // left unrotated is not orthogonal to the others once normalised (its direction is then
-  // dominated by leakage along the leading eigenvectors).
-  ja.noise_rel = SUB_NOISE_REL;
+  // Columns under the noise floor are not rotated (their near-degenerate directions would
+  // keep the tournament busy for nothing); sub_complete_kernel makes them orthonormal to the
+  // rest afterwards, so the next step's basis is orthonormal.
+  ja.noise_rel = NOISE_REL;
   ja.max_sweeps = max_sweeps;
   ja.tol = fmaxf(1e-6f, 8.0f * sqrtf((float)e.ldw) * 5.96e-8f);
   ja.rot_tol = 0.25f * ja.tol;
@@ -1164,11 +1273,12 @@ hipError_t run_eig_subspace(const double* SX, const double* SG, double inv_nx, d
       return err;
     hipLaunchKernelGGL(colnorm_kernel, dim3(m, 2), dim3(64), 0, st, sd, e.ldw, L);
     hipLaunchKernelGGL(frob_alive_kernel, dim3(2), dim3(1024), 0, st, sd, scale, m, m, flags + F_NALIVE,
-                       SUB_NOISE_REL);
+                       NOISE_REL);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     err = hipLaunchCooperativeKernel((const void*)jacobi_kernel, dim3(nb), dim3(JT), kargs, dyn, st);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(sub_normalize_kernel, dim3(m, 2), dim3(256), 0, st, sd, b.res[0], b.res[1], e.ldw);
+    hipLaunchKernelGGL(sub_normalize_kernel, dim3(m, 2), dim3(256), 0, st, sd, scale, b.res[0], b.res[1], e.ldw);
+    hipLaunchKernelGGL(sub_complete_kernel, dim3(2), dim3(SUB_CT), 0, st, sd, scale, m, L, e.ldw);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
 
