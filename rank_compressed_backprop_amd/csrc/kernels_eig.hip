@@ -1205,7 +1205,8 @@ __global__ __launch_bounds__(SUB_CT) void sub_complete_kernel(EigSides a, const 
 hipError_t run_eig_subspace(const double* SX, const double* SG, double inv_nx, double inv_ng, int L, int m,
                             int iters, int max_sweeps, bool warm, void* work, const EigOut& out,
                             int host_flags[EIG_HOST_FLAGS], hipStream_t st, bool wait) {
-  if (L > JAC_MAX_LDW || m < 16 || m % 16 || m >= L || iters < 1) return hipErrorInvalidValue;
+  // (sub_complete_kernel sorts at most 128 columns into its shared lists)
+  if (L > JAC_MAX_LDW || m < 16 || m % 16 || m >= L || m > 128 || iters < 1) return hipErrorInvalidValue;
   const EigLayout e = eig_layout(L);
   const EigBufs b = eig_bufs(work, e);
   int* flags = b.flags;
