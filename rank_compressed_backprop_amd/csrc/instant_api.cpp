@@ -76,7 +76,7 @@ bool config_ok(const instant_config* c) {
 
 struct Layout {
   size_t SX, SG, zpad, part, part_x_tiles, eig, sig_x, sig_g, info, rank, P32[2], Q32[2], PQ[2], Qt[2], Pgy, Qgy,
-      gxh, total;
+      gxh, gpart, gpart_floats, total;
   int ldL;
 };
 
@@ -107,6 +107,14 @@ Layout layout_of(const instant_config* c) {
     l.Q32[b] = take((size_t)c->R_max * L * sizeof(float));
     l.PQ[b] = take((size_t)2 * c->R_max * l.ldL * esz);
     l.Qt[b] = take(L * LD_QT * esz);
+  }
+  // float32 K-slice partials of g_hat_x = (Q gy) w when w is too large for L2 (M = B Ry rows)
+  {
+    size_t need = 0;
+    for (int m = 1; m <= c->B_max * c->R_max; ++m)
+      need = std::max(need, (size_t)gemm_ws_slices(c->dtype == INSTANT_BF16, false, m, c->Cx, c->Cy) * m * c->Cx);
+    l.gpart_floats = need;
+    l.gpart = take(need * sizeof(float));
   }
   l.Pgy = take((size_t)c->B_max * c->R_max * c->Cy * esz);
   l.Qgy = take((size_t)c->B_max * c->R_max * c->Cy * esz);
@@ -399,7 +407,9 @@ INSTANT_API instant_status instant_backward(instant_layer* h, const void* xhat, 
     // g_w = sum_b (P gy_b)^T x_hat_b: M = Cy, N = Cx, K = B * Rx
     if (e == hipSuccess) e = launch_gemm(h->bf16, true, Pgy, Cy, 0, xhat, Cx, 0, gw, Cx, 0, 1, Cy, Cx, B * Rx, st);
     // g_hat_x = (Q gy) w: M = B * Ry, N = Cx, K = Cy
-    if (e == hipSuccess) e = launch_gemm(h->bf16, false, Qgy, Cy, 0, w, Cx, 0, gxh, Cx, 0, 1, B * Ry, Cx, Cy, st);
+    if (e == hipSuccess)
+      e = launch_gemm(h->bf16, false, Qgy, Cy, 0, w, Cx, 0, gxh, Cx, 0, 1, B * Ry, Cx, Cy, st,
+                      (float*)(h->ws + h->lay.gpart), h->lay.gpart_floats, h->ws + h->lay.zpad);
     // g_x_b = Q^T g_hat_x_b
     if (e == hipSuccess) e = launch_expand(h->bf16, h->Qt(a), LD_QT, gxh, B, Ry, L, Cx, gx, st);
   }

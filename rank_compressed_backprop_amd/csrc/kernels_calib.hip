@@ -6,6 +6,7 @@
 //   build_io        I/O-dtype copies of the published projections
 // The eigen-decomposition and truncation live in kernels_eig.hip.
 #include "common.hpp"
+#include "dma.hpp"
 #include "launch.hpp"
 
 namespace instant {
@@ -43,38 +44,6 @@ __device__ inline void upper_tile(int idx, int T, int& ti, int& tj) {
     ++ti;
   }
   tj = ti + idx;
-}
-
-// 16 bytes per lane from src straight into LDS at lds_wave + 16 * lane (lds_wave uniform
-// across the wave). Kept out of the kernel body: target builtins there would keep the host
-// pass from emitting the kernel's launch stub.
-__device__ inline void lds_dma16(const void* src, void* lds_wave) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave, 16, 0, 0);
-}
-
-// Workgroup barrier without a memory fence (waits are explicit around it).
-__device__ inline void bare_barrier() {
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
-
-// Wait until at most N vector-memory loads of this wave are outstanding, and for all of its
-// LDS reads: the next barrier may hand their buffer to a refill.
-template <int N>
-__device__ inline void wait_vmcnt() {
-  __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
-}
-
-// Wait for the oldest stage when `younger` (0..Y) later stages of LDPS loads each may stay
-// in flight (the count has to be an immediate).
-template <int LDPS, int Y>
-__device__ inline void wait_oldest_stage(int younger) {
-  if constexpr (Y == 0) {
-    wait_vmcnt<0>();
-  } else {
-    if (younger >= Y) wait_vmcnt<Y * LDPS>();
-    else wait_oldest_stage<LDPS, Y - 1>(younger);
-  }
 }
 
 constexpr int WPANEL = ST * 128;  // bytes per panel of a stage

@@ -9,6 +9,7 @@
 #include <algorithm>
 
 #include "common.hpp"
+#include "dma.hpp"
 #include "launch.hpp"
 
 namespace instant {
@@ -139,6 +140,109 @@ __global__ __launch_bounds__(NW * WAVE) __attribute__((amdgpu_waves_per_eu(WPE, 
   __shared__ float red[NW][8][4][WAVE];
   gemm_block<T, A_TRANS, MT, NW, U, NT>(A, lda, strideA, Bm, ldb, strideB, Cm, ldc, strideC, M, N, K, blockIdx.x,
                                         blockIdx.y, blockIdx.z, threadIdx.x / WAVE, red);
+}
+
+// ---------------------------------------------------------------- g_hat_x with w read once
+// C[M][N] = A[M][K] . B[K][N] (A k-contiguous) for a B too large to stay in L2 and few rows
+// (g_hat_x = (Q gy) w of an LLM MLP: M = B*Ry = 272, w 90 MB). Blocks computing different row
+// ranges of one column strip would each stream the strip from memory again, so a block here
+// owns all M rows of a 128-column strip over one K slice (grid: strips x S). A stage (one
+// k-step: 32 rows of B x 128 columns, and the row tiles of A x 32 k) goes to LDS by DMA,
+// each wave issuing the same 1 + TPW loads (so its wait counts are exact); eight waves own
+// the row tiles w, w + 8, ...; the slices write float32 partials [S][M][N], which
+// splitk_reduce_kernel sums in slice order. K % 32 == 0, N % 8 == 0, M <= 128 * TPW.
+template <int TPW, int STG>
+__global__ __launch_bounds__(512) void gemm_ws_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ Bm,
+                                                      int ldb, float* __restrict__ part, int M, int N, int K,
+                                                      const bf16* __restrict__ zpad) {
+  typedef MM<bf16> mm;
+  typedef mm::frag frag;
+  constexpr int NT = 8 * TPW;             // row tile slots of a stage
+  constexpr int STAGE = 1024 * (8 + NT);  // bytes: B chunks [g][lane], then A tiles [t][lane]
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[STG][STAGE];
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int z = blockIdx.y, S = gridDim.y;
+  const int col = blockIdx.x * 128 + 8 * (lane & 15);
+  const bool col_ok = col < N;
+  const int kl = 8 * (lane >> 4);
+  const int nsteps = K / mm::KSTEP;
+  const int sb = (int)((long)nsteps * z / S), se = (int)((long)nsteps * (z + 1) / S), nq = se - sb;
+  // B chunk g = wave: rows k0 + g of the lanes' columns; A tile t = wave + 8j: rows 16t + lane % 16
+  auto issue = [&](int s, int slot) {
+    const int k0 = s * mm::KSTEP + kl;
+    unsigned char* st = ring[slot];
+    lds_dma16(col_ok ? (const void*)(Bm + (size_t)(k0 + wave) * ldb + col) : (const void*)zpad, st + 1024 * wave);
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int t = wave + 8 * j;
+      const int m = 16 * t + (lane & 15);
+      lds_dma16(m < M ? (const void*)(A + (size_t)m * lda + k0) : (const void*)zpad, st + 1024 * (8 + t));
+    }
+  };
+  f32x4 acc[TPW][8];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[j][u] = zero4();
+#pragma unroll
+  for (int q = 0; q < STG - 1; ++q)
+    if (q < nq) issue(sb + q, q);
+  for (int i = 0; i < nq; ++i) {
+    // stage i has landed once at most the later stages' loads remain (and LDS reads are done)
+    const int later = (nq - 1 - i) < (STG - 2) ? (nq - 1 - i) : (STG - 2);
+    wait_oldest_stage<1 + TPW, STG - 2>(later);
+    bare_barrier();  // every wave's part of stage i; every read of the buffer refilled next
+    if (i + STG - 1 < nq) issue(sb + i + STG - 1, (i + STG - 1) % STG);
+    const unsigned char* st = ring[i % STG];
+    bf16x8 r[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) r[g] = *reinterpret_cast<const bf16x8*>(st + 1024 * g + 16 * lane);
+    frag bf[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int g = 0; g < 8; ++g) bf[u][g] = r[g][u];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const frag af = *reinterpret_cast<const frag*>(st + 1024 * (8 + wave + 8 * j) + 16 * lane);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[j][u] = mm::mma(af, bf[u], acc[j][u]);
+    }
+  }
+  float* __restrict__ out = part + (size_t)z * M * N;
+#pragma unroll
+  for (int j = 0; j < TPW; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = 16 * (wave + 8 * j) + 4 * (lane >> 4) + v;
+      if (m < M && col_ok) {
+        float* p = out + (size_t)m * N + col;
+        *reinterpret_cast<f32x4*>(p) = f32x4{acc[j][0][v], acc[j][1][v], acc[j][2][v], acc[j][3][v]};
+        *reinterpret_cast<f32x4*>(p + 4) = f32x4{acc[j][4][v], acc[j][5][v], acc[j][6][v], acc[j][7][v]};
+      }
+    }
+}
+
+// C[m][n] = sum_{z < S} part[z][m][n] in slice order (part: S slices of [M][N] float32).
+template <class T>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S, int M, int N,
+                                                            T* __restrict__ Cm, int ldc) {
+  const int n4 = N / 4;
+  const size_t slice = (size_t)M * N;
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < (size_t)M * n4; e += (size_t)gridDim.x * 256) {
+    const int m = (int)(e / n4), c = (int)(e % n4) * 4;
+    const float* p = part + (size_t)m * N + c;
+    f32x4 acc = *reinterpret_cast<const f32x4*>(p);
+    for (int z = 1; z < S; ++z) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p + z * slice);
+      acc[0] += v[0];
+      acc[1] += v[1];
+      acc[2] += v[2];
+      acc[3] += v[3];
+    }
+    const float o[4] = {acc[0], acc[1], acc[2], acc[3]};
+    store_row<T, 4>(Cm + (size_t)m * ldc + c, o);
+  }
 }
 
 // ----------------------------------------------------------------------------- expand
@@ -388,12 +492,39 @@ static hipError_t gemm_cfg(const void* A, int lda, size_t sA, const void* Bm, in
   return hipGetLastError();
 }
 
+constexpr int WS_TPW = 3;  // row tiles per wave of gemm_ws_kernel: up to 384 rows
+
+int gemm_ws_slices(bool bf16_io, bool a_trans, int M, int N, int K) {
+  if (!bf16_io || a_trans || M < 1 || M > 128 * WS_TPW || K % 32 || N % 8) return 0;
+  if ((double)N * K * 2 < 32.0 * (1 << 20)) return 0;  // B small enough to stay in L2: the row blocks share it
+  const int strips = (N + 127) / 128;
+  int S = std::max(2, std::min(16, 256 / strips));      // about one block per compute unit
+  S = std::min(S, (K / 32) / 16);                        // slices of at least 16 k-steps
+  return S >= 2 ? S : 0;
+}
+
 template <class T, bool AT>
 static hipError_t gemm_t(const void* A, int lda, size_t sA, const void* Bm, int ldb, size_t sB, void* Cm, int ldc,
-                         size_t sC, int batch, int M, int N, int K, hipStream_t st) {
+                         size_t sC, int batch, int M, int N, int K, float* part, size_t part_floats,
+                         const void* zpad, hipStream_t st) {
   const int nsteps = (K + MM<T>::KSTEP - 1) / MM<T>::KSTEP;
   constexpr bool BF = MM<T>::KSTEP == 32;
   const long strips = (N + 127) / 128;
+  if constexpr (BF && !AT) {
+    // (bf16, measured on gfx950) B read once when it is too large for L2 (LLM MLP g_hat_x,
+    // 272 x 4096 x 11008: 55.5 us against 71.7 us for row blocks that each stream w again)
+    const int S = (part && zpad && batch == 1) ? gemm_ws_slices(true, false, M, N, K) : 0;
+    if (S && (size_t)S * M * N <= part_floats) {
+      hipLaunchKernelGGL((gemm_ws_kernel<WS_TPW, 3>), dim3((unsigned)strips, S), dim3(512), 0, st, (const bf16*)A, lda,
+                         (const bf16*)Bm, ldb, part, M, N, K, (const bf16*)zpad);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const size_t n4 = (size_t)M * (N / 4);
+      hipLaunchKernelGGL(splitk_reduce_kernel<T>, dim3((unsigned)std::min<size_t>((n4 + 255) / 256, 2048)), dim3(256),
+                         0, st, (const float*)part, S, M, N, (T*)Cm, ldc);
+      return hipGetLastError();
+    }
+  }
   if constexpr (AT) {
     if constexpr (BF) {
       // (bf16, measured on gfx950) Many 64x128 tiles (g_w of an LLM MLP: 5504 at 11008 x 4096,
@@ -432,12 +563,15 @@ static hipError_t gemm_t(const void* A, int lda, size_t sA, const void* Bm, int 
 }
 
 hipError_t launch_gemm(bool bf16_io, bool a_trans, const void* A, int lda, size_t sA, const void* Bm, int ldb,
-                       size_t sB, void* Cm, int ldc, size_t sC, int batch, int M, int N, int K, hipStream_t st) {
+                       size_t sB, void* Cm, int ldc, size_t sC, int batch, int M, int N, int K, hipStream_t st,
+                       float* part, size_t part_floats, const void* zpad) {
   if (bf16_io)
-    return a_trans ? gemm_t<bf16, true>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st)
-                   : gemm_t<bf16, false>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
-  return a_trans ? gemm_t<float, true>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st)
-                 : gemm_t<float, false>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, st);
+    return a_trans
+               ? gemm_t<bf16, true>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, part, part_floats, zpad, st)
+               : gemm_t<bf16, false>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, part, part_floats, zpad, st);
+  return a_trans
+             ? gemm_t<float, true>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, part, part_floats, zpad, st)
+             : gemm_t<float, false>(A, lda, sA, Bm, ldb, sB, Cm, ldc, sC, batch, M, N, K, part, part_floats, zpad, st);
 }
 
 template <class T, int KS>

@@ -16,8 +16,13 @@ hipError_t launch_proj(bool bf16_io, const void* A, int ldA, int M, int M0, cons
 
 // Cm[m][n] = sum_k A(m,k) B[k][n] per batch entry z (pointer strides sA, sB, sC in
 // elements). a_trans: A stored [K][lda] instead of [M][lda]. M, N multiples of 4 / 8.
+// part (room for part_floats float32) and zpad (16 zero bytes in device memory), when given,
+// let a bf16 GEMM whose B is too large for L2 read B once over K slices (gemm_ws_slices).
 hipError_t launch_gemm(bool bf16_io, bool a_trans, const void* A, int lda, size_t sA, const void* Bm, int ldb,
-                       size_t sB, void* Cm, int ldc, size_t sC, int batch, int M, int N, int K, hipStream_t st);
+                       size_t sB, void* Cm, int ldc, size_t sC, int batch, int M, int N, int K, hipStream_t st,
+                       float* part = nullptr, size_t part_floats = 0, const void* zpad = nullptr);
+// K slices (0: not used) of that path for these shapes; it needs S * M * N floats of part.
+int gemm_ws_slices(bool bf16_io, bool a_trans, int M, int N, int K);
 
 // Out[b][l][c] = sum_{r<R} At[l][r] Bz[b][r][c]; At: [L][ldA], zero beyond column R.
 hipError_t launch_expand(bool bf16_io, const void* At, int ldA, const void* Bz, int B, int R, int L, int C,

@@ -75,6 +75,9 @@ RAGGED = [
     # more g_w tiles than the compute units the g_x strips leave free (256 of them): some
     # blocks take two tiles, an odd count of them
     ("bf16", 40, 33, 264, 2952, 5, 9),
+    # w (1544 x 11008, 34 MB) too large for L2: g_hat_x reads it once over K slices, with a
+    # partial last column strip and a row count (3 * 23) that fills no whole tile
+    ("bf16", 3, 70, 1544, 11008, 19, 23),
 ]
 
 
