@@ -85,7 +85,9 @@ struct EigBufs {
   int* version;     // [2][nb]
   int* cols[2];     // [ncols] column order: columns above the noise floor first
   float* res[2];    // subspace solver: Ritz residual ||C v_c - sigma_c v_c|| per column
+  double* frob;     // subspace solver: per-block sums of ||C||_F^2 [2][SUB_FROB_BLOCKS]
 };
+constexpr size_t EIG_FROB_BYTES = 2 * 64 * sizeof(double);  // [2][SUB_FROB_BLOCKS]
 
 static EigBufs eig_bufs(void* work, const EigLayout& e) {
   EigBufs b;
@@ -121,12 +123,15 @@ static EigBufs eig_bufs(void* work, const EigLayout& e) {
   b.res[0] = (float*)p;
   p += e.nrmbytes;
   b.res[1] = (float*)p;
+  p += e.nrmbytes;
+  b.frob = (double*)p;
   return b;
 }
 
 size_t eig_workspace_bytes(int L) {
   const EigLayout e = eig_layout(L);
-  return 6 * e.wbytes + 2 * e.vbytes + 4 * e.nrmbytes + EIG_FLAGS_BYTES + e.verbytes + 2 * e.colbytes;
+  return 6 * e.wbytes + 2 * e.vbytes + 4 * e.nrmbytes + EIG_FLAGS_BYTES + e.verbytes + 2 * e.colbytes +
+         EIG_FROB_BYTES;
 }
 
 // ---------------------------------------------------------------------------- set-up kernels
@@ -1018,27 +1023,39 @@ int eig_subspace_width(int L, int R_max) {
 }
 
 // ||C||_F^2 = sum_i C_ii^2 + 2 sum_{i<j} C_ij^2 from the float64 upper-triangle sums, in a
-// fixed order (one block per side).
-__global__ __launch_bounds__(1024) void stat_frob_kernel(EigSides a, int L, double* __restrict__ out) {
-  __shared__ double part[1024];
-  const int side = blockIdx.x;
+// fixed order: block b of a side takes the rows i = b mod SUB_FROB_BLOCKS and writes its sum
+// to part[side][b]; stat_frob_fold_kernel adds those in block order.
+constexpr int SUB_FROB_BLOCKS = 64;
+static_assert(EIG_FROB_BYTES == 2 * SUB_FROB_BLOCKS * sizeof(double), "per-block energy sums");
+__global__ __launch_bounds__(256) void stat_frob_kernel(EigSides a, int L, double* __restrict__ part) {
+  __shared__ double red[256];
+  const int side = blockIdx.y, b = blockIdx.x;
   const double* S = a.S[side];
   const double inv = a.inv[side];
   double acc = 0.0;
-  for (int i = 0; i < L; ++i) {
+  for (int i = b; i < L; i += SUB_FROB_BLOCKS) {
     const double* row = S + (size_t)i * L;
-    for (int j = i + threadIdx.x; j < L; j += 1024) {
+    for (int j = i + threadIdx.x; j < L; j += 256) {
       const double v = row[j] * inv;
       acc += (j == i ? 1.0 : 2.0) * v * v;
     }
   }
-  part[threadIdx.x] = acc;
+  red[threadIdx.x] = acc;
   __syncthreads();
-  for (int st = 512; st > 0; st >>= 1) {
-    if (threadIdx.x < st) part[threadIdx.x] += part[threadIdx.x + st];
+  for (int st = 128; st > 0; st >>= 1) {
+    if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
     __syncthreads();
   }
-  if (threadIdx.x == 0) out[side] = part[0];
+  if (threadIdx.x == 0) part[side * SUB_FROB_BLOCKS + b] = red[0];
+}
+
+__global__ void stat_frob_fold_kernel(const double* __restrict__ part, double* __restrict__ out) {
+  const int side = threadIdx.x;
+  if (side < 2) {
+    double e = 0.0;
+    for (int b = 0; b < SUB_FROB_BLOCKS; ++b) e += part[side * SUB_FROB_BLOCKS + b];
+    out[side] = e;
+  }
 }
 
 // Pseudo-random starting basis (a counter-based hash of row, column and side, uniform in
@@ -1109,6 +1126,7 @@ __global__ __launch_bounds__(SUB_CT) void sub_complete_kernel(EigSides a, const 
   __shared__ int n_live, n_dead;
   __shared__ double coef[128 * SUB_MAX_DEAD];
   __shared__ double gl[SUB_MAX_DEAD * SUB_MAX_DEAD];  // Gram matrix, then its Cholesky factor
+  __shared__ double li[SUB_MAX_DEAD * SUB_MAX_DEAD];  // inverse of the Cholesky factor (lower)
   const int side = blockIdx.x, tid = threadIdx.x;
   float* __restrict__ V = a.V32[side];
   if (tid == 0) {
@@ -1188,16 +1206,34 @@ __global__ __launch_bounds__(SUB_CT) void sub_complete_kernel(EigSides a, const 
       if (tid == 0) gl[j * SUB_MAX_DEAD + j] = ljj;
       __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
+    // column c of L^-1 by forward substitution (lane c); a zero pivot zeroes its row
+    if (tid < nd) {
+      const int c = tid;
+      for (int i = 0; i < nd; ++i) {
+        double x = 0.0;
+        if (i >= c) {
+          x = i == c ? 1.0 : 0.0;
+          for (int k = c; k < i; ++k) x -= gl[i * SUB_MAX_DEAD + k] * li[k * SUB_MAX_DEAD + c];
+          const double lii = gl[i * SUB_MAX_DEAD + i];
+          x = lii > 0.0 ? x / lii : 0.0;
+        }
+        li[i * SUB_MAX_DEAD + c] = x;
+      }
+    }
   }
   __syncthreads();
-  // rows of the dead block times L^-T: forward substitution per row
-  // (a thread solves its own rows: the solved entries it reads back are its own stores)
+  // rows of the dead block times L^-T
+  // (every load of a row before any store, so the loads of a row go out together)
   for (int r = tid; r < L; r += SUB_CT) {
+    double v[SUB_MAX_DEAD];
+#pragma unroll
+    for (int d = 0; d < SUB_MAX_DEAD; ++d) v[d] = d < nd ? (double)V[(size_t)dead_c[d] * ldw + r] : 0.0;
     for (int d = 0; d < nd; ++d) {
-      double v = (double)V[(size_t)dead_c[d] * ldw + r];
-      for (int k = 0; k < d; ++k) v -= gl[d * SUB_MAX_DEAD + k] * (double)V[(size_t)dead_c[k] * ldw + r];
-      const double ldd = gl[d * SUB_MAX_DEAD + d];
-      V[(size_t)dead_c[d] * ldw + r] = ldd > 0.0 ? (float)(v / ldd) : 0.0f;
+      double y = 0.0;
+#pragma unroll
+      for (int k = 0; k < SUB_MAX_DEAD; ++k)  // (constant k: v stays in registers)
+        if (k <= d) y += li[d * SUB_MAX_DEAD + k] * v[k];
+      V[(size_t)dead_c[d] * ldw + r] = (float)y;
     }
   }
 }
@@ -1228,7 +1264,8 @@ hipError_t run_eig_subspace(const double* SX, const double* SG, double inv_nx, d
     sd.cols[s] = b.cols[s];
   }
   hipLaunchKernelGGL(jacobi_prep_kernel, dim3(e.ncols, 2), dim3(256), 0, st, sd, L, e.ldw, 0, flags + F_BAD);
-  hipLaunchKernelGGL(stat_frob_kernel, dim3(2), dim3(1024), 0, st, sd, L, eexact);
+  hipLaunchKernelGGL(stat_frob_kernel, dim3(SUB_FROB_BLOCKS, 2), dim3(256), 0, st, sd, L, b.frob);
+  hipLaunchKernelGGL(stat_frob_fold_kernel, dim3(1), dim3(64), 0, st, (const double*)b.frob, eexact);
   if (!warm) hipLaunchKernelGGL(seed_basis_kernel, dim3(m, 2), dim3(256), 0, st, sd, L, e.ldw);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
