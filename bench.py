@@ -191,6 +191,9 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # every successful finalize publishes one new generation of projections; an asynchronous
+    # one that fails is only seen here (the old projections stay in use)
+    gen0 = lay.query()[1].generation
     t0 = time.perf_counter()
     for i in range(args.warmup, args.warmup + args.steps):
         step(i, timed=True)
@@ -198,6 +201,10 @@ def main():
     wall = time.perf_counter() - t0
     fin_loop = [a.elapsed_time(b) * 1e-3 for a, b in fin_events]
     _, info = lay.query()
+    published = info.generation - gen0
+    if published != len(fin_events):
+        print(f"warning: {len(fin_events) - published} of {len(fin_events)} finalizes in the timed loop "
+              "published no projections", file=sys.stderr)
     Rx, Ry = info.Rx, info.Ry
 
     # ---- per-part timing with HIP events on the launch stream, right after the timed loop.
@@ -291,6 +298,7 @@ def main():
             "finalize_in_loop_ms": (sum(fin_loop) / len(fin_loop) * 1e3) if fin_loop else None,
             "finalizes_in_loop": len(fin_loop), "host_enqueue_us_per_plain_step": t_issue * 1e6, "jacobi_sweeps": [info2.sweeps_x, info2.sweeps_g],
             "finalize_status": rcb.instant_status_str(s),
+            "finalizes_published": f"{published}/{len(fin_events)}",
         },
         "roofline": {"kernel": "proj (forward compression x_hat = P x)", "bound": "hbm",
                      "achieved": gbs_fwd, "peak": HBM_PEAK_GBS, "unit": "GB/s",

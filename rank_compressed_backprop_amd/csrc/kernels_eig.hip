@@ -86,8 +86,23 @@ struct EigBufs {
   int* cols[2];     // [ncols] column order: columns above the noise floor first
   float* res[2];    // subspace solver: Ritz residual ||C v_c - sigma_c v_c|| per column
   double* frob;     // subspace solver: per-block sums of ||C||_F^2 [2][SUB_FROB_BLOCKS]
+  struct SubScratch* sub;  // subspace solver: basis completion, one per side
 };
 constexpr size_t EIG_FROB_BYTES = 2 * 64 * sizeof(double);  // [2][SUB_FROB_BLOCKS]
+
+// Basis completion of the subspace solver (per side): the column lists, the Gram-Schmidt
+// coefficients of the live columns against the completed (dead) ones, the dead columns'
+// Gram matrix and the inverse of its Cholesky factor.
+constexpr int SUB_MAX_COLS = 128;  // widest basis the subspace solver takes
+constexpr int SUB_MAX_DEAD = 32;   // near-null basis columns completed per side and step (the rest are zeroed)
+struct SubScratch {
+  double coef[SUB_MAX_COLS * SUB_MAX_DEAD];  // [live j][dead d]
+  double gram[SUB_MAX_DEAD * SUB_MAX_DEAD];  // [dead i][dead d]
+  double li[SUB_MAX_DEAD * SUB_MAX_DEAD];    // inverse of the lower Cholesky factor, [row][col]
+  int nl, nd_all;                            // live columns; dead columns (of which at most SUB_MAX_DEAD completed)
+  int live[SUB_MAX_COLS], dead[SUB_MAX_COLS];
+};
+constexpr size_t EIG_SUB_BYTES = 2 * ((sizeof(SubScratch) + 255) / 256 * 256);
 
 static EigBufs eig_bufs(void* work, const EigLayout& e) {
   EigBufs b;
@@ -125,13 +140,15 @@ static EigBufs eig_bufs(void* work, const EigLayout& e) {
   b.res[1] = (float*)p;
   p += e.nrmbytes;
   b.frob = (double*)p;
+  p += EIG_FROB_BYTES;
+  b.sub = (SubScratch*)p;  // EIG_SUB_BYTES: two of them, 256-byte aligned
   return b;
 }
 
 size_t eig_workspace_bytes(int L) {
   const EigLayout e = eig_layout(L);
   return 6 * e.wbytes + 2 * e.vbytes + 4 * e.nrmbytes + EIG_FLAGS_BYTES + e.verbytes + 2 * e.colbytes +
-         EIG_FROB_BYTES;
+         EIG_FROB_BYTES + EIG_SUB_BYTES;
 }
 
 // ---------------------------------------------------------------------------- set-up kernels
@@ -1014,8 +1031,6 @@ int eig_max_L() { return JAC_MAX_LDW; }
 // finalize starts the next; the first starts from pseudo-random columns.
 
 constexpr float SUB_RES_TOL = 3e-5f;  // kept Ritz residuals, relative to sigma_0
-constexpr int SUB_MAX_DEAD = 32;  // near-null basis columns completed per side and step (the rest are zeroed)
-constexpr int SUB_CT = 1024;      // threads of the completion kernel (latency-bound: as many waves as fit)
 
 int eig_subspace_width(int L, int R_max) {
   const int m = (R_max + 16 + 15) / 16 * 16;  // 16 more directions than the largest rank, whole blocks
@@ -1090,7 +1105,7 @@ __global__ __launch_bounds__(256) void sub_reset_kernel(EigSides a, int* __restr
 
 // After each Jacobi launch: the new basis u_c = W[:, c] / sigma_c and the Ritz residual
 // sigma_c ||u_c - (V J)_c||. Columns under the noise floor were not rotated: their basis
-// column stays as it was, for sub_complete_kernel to make orthogonal to the new one.
+// column stays as it was, for the completion kernels to make orthogonal to the new one.
 __global__ __launch_bounds__(256) void sub_normalize_kernel(EigSides a, const double* __restrict__ scale, float* res0,
                                                             float* res1, int ldw) {
   __shared__ double part[256];
@@ -1114,135 +1129,200 @@ __global__ __launch_bounds__(256) void sub_normalize_kernel(EigSides a, const do
   if (threadIdx.x == 0) (s ? res1 : res0)[c] = sig * (float)sqrt(part[0]);
 }
 
-// Completes the basis after a step (one block per side): the columns under the noise floor
-// (whose directions carry no energy, so any orthonormal completion will do) are made
-// orthogonal to the live columns by two passes of classical Gram-Schmidt, then orthonormal
-// among themselves by a Cholesky factorisation of their Gram matrix, all in float64. A
-// column that falls into the span of the others, and every dead column beyond
-// SUB_MAX_DEAD, becomes zero; a zero column stays zero (C 0 = 0) and is never kept.
-__global__ __launch_bounds__(SUB_CT) void sub_complete_kernel(EigSides a, const double* __restrict__ scale, int m,
-                                                            int L, int ldw) {
-  __shared__ int live_c[128], dead_c[128];
-  __shared__ int n_live, n_dead;
-  __shared__ double coef[128 * SUB_MAX_DEAD];
-  __shared__ double gl[SUB_MAX_DEAD * SUB_MAX_DEAD];  // Gram matrix, then its Cholesky factor
-  __shared__ double li[SUB_MAX_DEAD * SUB_MAX_DEAD];  // inverse of the Cholesky factor (lower)
-  const int side = blockIdx.x, tid = threadIdx.x;
-  float* __restrict__ V = a.V32[side];
-  if (tid == 0) {
-    int nl = 0, nd = 0;
-    const double floor_g = NOISE_REL * scale[side];
-    for (int c = 0; c < m; ++c) {
-      const double sg = (double)a.nrm[side][c];
-      if (sg * sg > floor_g) live_c[nl++] = c;
-      else dead_c[nd++] = c;
-    }
-    n_live = nl;
-    n_dead = nd;
+// Basis completion after a step. The columns under the noise floor ("dead": their
+// directions carry no energy, so any orthonormal completion will do) are made orthogonal to
+// the live columns by two passes of classical Gram-Schmidt, then orthonormal among
+// themselves through the Cholesky factor of their Gram matrix, all in float64. A column
+// that falls into the span of the others, and every dead column beyond SUB_MAX_DEAD, becomes
+// zero; a zero column stays zero (C 0 = 0) and is never kept. The work is spread over many
+// compute units in five short kernels: lists, dots (one block per column), row updates and
+// the row transform (blocks of rows), and the factorisation (one wave per side).
+
+// Column lists from the norms the Jacobi left: live columns in index order, then dead ones.
+__global__ void sub_lists_kernel(EigSides a, const double* __restrict__ scale, int m, SubScratch* __restrict__ sub) {
+  const int side = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  SubScratch& S = sub[side];
+  const double floor_g = NOISE_REL * scale[side];
+  int nl = 0, nd = 0;
+  for (int c = 0; c < m; ++c) {
+    const double sg = (double)a.nrm[side][c];
+    if (sg * sg > floor_g) S.live[nl++] = c;
+    else S.dead[nd++] = c;
   }
+  S.nl = nl;
+  S.nd_all = nd;
+}
+
+// Dots of one column against every completed dead column: block j takes live column j
+// (gram = 0, the Gram-Schmidt coefficients) or dead column j (gram = 1, the Gram matrix).
+// Each thread sums its rows in order, each wave by a fixed shuffle tree, the waves in order.
+constexpr int SUB_DT = 256;
+__global__ __launch_bounds__(SUB_DT) void sub_dots_kernel(EigSides a, SubScratch* __restrict__ sub, int gram, int L,
+                                                          int ldw) {
+  const int side = blockIdx.y, j = blockIdx.x;
+  SubScratch& S = sub[side];
+  const int nd = S.nd_all < SUB_MAX_DEAD ? S.nd_all : SUB_MAX_DEAD;
+  const int cnt = gram ? nd : S.nl;
+  if (nd == 0 || j >= cnt) return;
+  __shared__ int dl[SUB_MAX_DEAD];
+  if (threadIdx.x < SUB_MAX_DEAD) dl[threadIdx.x] = threadIdx.x < nd ? S.dead[threadIdx.x] : 0;
   __syncthreads();
-  const int nl = n_live, nd_all = n_dead;
-  if (nd_all == 0) return;
-  const int nd = nd_all < SUB_MAX_DEAD ? nd_all : SUB_MAX_DEAD;
-  for (int i = nd; i < nd_all; ++i)
-    for (int r = tid; r < L; r += SUB_CT) V[(size_t)dead_c[i] * ldw + r] = 0.0f;
-  const int lane = tid & (WAVE - 1), wave = tid / WAVE;
-  constexpr int NWAVE = SUB_CT / WAVE;
-  // dots of one column x against every dead column at once (float64, fixed order): the
-  // loads of a row are independent, so a wave keeps many of them in flight
-  auto dots_vs_dead = [&](const float* x, double* out) {
-    double acc[SUB_MAX_DEAD];
+  const float* __restrict__ V = a.V32[side];
+  const float* __restrict__ x = V + (size_t)(gram ? S.dead[j] : S.live[j]) * ldw;
+  double acc[SUB_MAX_DEAD];
 #pragma unroll
-    for (int d = 0; d < SUB_MAX_DEAD; ++d) acc[d] = 0.0;
-    for (int r = lane; r < L; r += WAVE) {
-      const double xr = (double)x[r];
+  for (int d = 0; d < SUB_MAX_DEAD; ++d) acc[d] = 0.0;
+  for (int r = threadIdx.x; r < L; r += SUB_DT) {
+    const double xr = (double)x[r];
 #pragma unroll
-      for (int d = 0; d < SUB_MAX_DEAD; ++d)
-        if (d < nd) acc[d] += xr * (double)V[(size_t)dead_c[d] * ldw + r];
-    }
+    for (int d = 0; d < SUB_MAX_DEAD; ++d)
+      if (d < nd) acc[d] += xr * (double)V[(size_t)dl[d] * ldw + r];
+  }
+  __shared__ double part[SUB_DT / WAVE][SUB_MAX_DEAD];
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
 #pragma unroll
-    for (int d = 0; d < SUB_MAX_DEAD; ++d) {
-      if (d >= nd) break;
+  for (int d = 0; d < SUB_MAX_DEAD; ++d) {
+    if (d < nd) {  // (the same for every lane; no early exit, so acc stays in registers)
       double v = acc[d];
+#pragma unroll
       for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-      if (lane == 0) out[d] = v;
+      if (lane == 0) part[wave][d] = v;
     }
-  };
-  // two passes: v_d -= sum_j (u_j . v_d) u_j over the live columns
+  }
+  __syncthreads();
+  if (threadIdx.x < nd) {
+    double v = part[0][threadIdx.x];
+    for (int w = 1; w < SUB_DT / WAVE; ++w) v += part[w][threadIdx.x];
+    (gram ? S.gram : S.coef)[j * SUB_MAX_DEAD + threadIdx.x] = v;
+  }
+}
+
+// One Gram-Schmidt pass over a block of rows: v_d -= sum_j coef[j][d] u_j, the live columns
+// in order, eight loads at a time.
+constexpr int SUB_RT = 256;
+__global__ __launch_bounds__(SUB_RT) void sub_update_kernel(EigSides a, SubScratch* __restrict__ sub, int L, int ldw) {
+  const int side = blockIdx.y;
+  SubScratch& S = sub[side];
+  const int nd = S.nd_all < SUB_MAX_DEAD ? S.nd_all : SUB_MAX_DEAD;
+  const int nl = S.nl;
+  if (nd == 0) return;
+  __shared__ double cf[SUB_MAX_COLS * SUB_MAX_DEAD];
+  for (int e = threadIdx.x; e < nl * SUB_MAX_DEAD; e += SUB_RT) cf[e] = S.coef[e];
+  __syncthreads();
+  const int r = blockIdx.x * SUB_RT + threadIdx.x;
+  if (r >= L) return;
+  float* __restrict__ V = a.V32[side];
+  double v[SUB_MAX_DEAD];
+#pragma unroll
+  for (int d = 0; d < SUB_MAX_DEAD; ++d) v[d] = d < nd ? (double)V[(size_t)S.dead[d] * ldw + r] : 0.0;
+  constexpr int JU = 8;
+  for (int j0 = 0; j0 < nl; j0 += JU) {
+    float u[JU];
+#pragma unroll
+    for (int q = 0; q < JU; ++q) u[q] = j0 + q < nl ? V[(size_t)S.live[j0 + q] * ldw + r] : 0.0f;
+#pragma unroll
+    for (int q = 0; q < JU; ++q) {
+      if (j0 + q >= nl) break;
+#pragma unroll
+      for (int d = 0; d < SUB_MAX_DEAD; ++d) v[d] -= cf[(j0 + q) * SUB_MAX_DEAD + d] * (double)u[q];
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < SUB_MAX_DEAD; ++d)
+    if (d < nd) V[(size_t)S.dead[d] * ldw + r] = (float)v[d];
+}
+
+// Cholesky factor of the dead columns' Gram matrix and its inverse, one wave per side.
+__global__ __launch_bounds__(WAVE) void sub_chol_kernel(SubScratch* __restrict__ sub) {
+  SubScratch& S = sub[blockIdx.x];
+  const int nd = S.nd_all < SUB_MAX_DEAD ? S.nd_all : SUB_MAX_DEAD;
+  if (nd == 0) return;
+  __shared__ double gl[SUB_MAX_DEAD * SUB_MAX_DEAD];
+  __shared__ double li[SUB_MAX_DEAD * SUB_MAX_DEAD];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < nd * SUB_MAX_DEAD; e += WAVE) gl[e] = S.gram[e];
+  __syncthreads();
+  for (int j = 0; j < nd; ++j) {
+    double sjj = gl[j * SUB_MAX_DEAD + j];
+    for (int k = 0; k < j; ++k) sjj -= gl[j * SUB_MAX_DEAD + k] * gl[j * SUB_MAX_DEAD + k];
+    // the columns had unit norm before the projections: a pivot this small means the column
+    // lies in the span of the others
+    const double ljj = sjj > 1e-8 ? sqrt(sjj) : 0.0;
+    for (int i = j + 1 + tid; i < nd; i += WAVE) {
+      double sij = gl[i * SUB_MAX_DEAD + j];
+      for (int k = 0; k < j; ++k) sij -= gl[i * SUB_MAX_DEAD + k] * gl[j * SUB_MAX_DEAD + k];
+      gl[i * SUB_MAX_DEAD + j] = ljj > 0.0 ? sij / ljj : 0.0;
+    }
+    if (tid == 0) gl[j * SUB_MAX_DEAD + j] = ljj;
+    __syncthreads();
+  }
+  // column c of L^-1 by forward substitution (lane c); a zero pivot zeroes its row
+  if (tid < nd) {
+    const int c = tid;
+    for (int i = 0; i < nd; ++i) {
+      double x = 0.0;
+      if (i >= c) {
+        x = i == c ? 1.0 : 0.0;
+        for (int k = c; k < i; ++k) x -= gl[i * SUB_MAX_DEAD + k] * li[k * SUB_MAX_DEAD + c];
+        const double lii = gl[i * SUB_MAX_DEAD + i];
+        x = lii > 0.0 ? x / lii : 0.0;
+      }
+      li[i * SUB_MAX_DEAD + c] = x;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < nd * SUB_MAX_DEAD; e += WAVE) S.li[e] = li[e];
+}
+
+// Rows of the completed dead block times L^-T (every load of a row before any store), and
+// the dead columns beyond SUB_MAX_DEAD set to zero.
+__global__ __launch_bounds__(SUB_RT) void sub_transform_kernel(EigSides a, SubScratch* __restrict__ sub, int L,
+                                                               int ldw) {
+  const int side = blockIdx.y;
+  SubScratch& S = sub[side];
+  const int nd_all = S.nd_all;
+  const int nd = nd_all < SUB_MAX_DEAD ? nd_all : SUB_MAX_DEAD;
+  if (nd == 0) return;
+  __shared__ double li[SUB_MAX_DEAD * SUB_MAX_DEAD];
+  for (int e = threadIdx.x; e < nd * SUB_MAX_DEAD; e += SUB_RT) li[e] = S.li[e];
+  __syncthreads();
+  const int r = blockIdx.x * SUB_RT + threadIdx.x;
+  if (r >= L) return;
+  float* __restrict__ V = a.V32[side];
+  for (int i = nd; i < nd_all; ++i) V[(size_t)S.dead[i] * ldw + r] = 0.0f;
+  double v[SUB_MAX_DEAD];
+#pragma unroll
+  for (int d = 0; d < SUB_MAX_DEAD; ++d) v[d] = d < nd ? (double)V[(size_t)S.dead[d] * ldw + r] : 0.0;
+  for (int d = 0; d < nd; ++d) {
+    double y = 0.0;
+#pragma unroll
+    for (int k = 0; k < SUB_MAX_DEAD; ++k)  // (constant k: v stays in registers)
+      if (k <= d) y += li[d * SUB_MAX_DEAD + k] * v[k];
+    V[(size_t)S.dead[d] * ldw + r] = (float)y;
+  }
+}
+
+static hipError_t launch_sub_complete(const EigSides& sd, const double* scale, SubScratch* sub, int m, int L, int ldw,
+                                      hipStream_t st) {
+  const dim3 rows((L + SUB_RT - 1) / SUB_RT, 2);
+  hipLaunchKernelGGL(sub_lists_kernel, dim3(2), dim3(WAVE), 0, st, sd, scale, m, sub);
   for (int pass = 0; pass < 2; ++pass) {
-    for (int j = wave; j < nl; j += NWAVE) dots_vs_dead(V + (size_t)live_c[j] * ldw, coef + j * SUB_MAX_DEAD);
-    __syncthreads();
-    for (int r = tid; r < L; r += SUB_CT) {
-      double v[SUB_MAX_DEAD];
-#pragma unroll
-      for (int d = 0; d < SUB_MAX_DEAD; ++d) v[d] = d < nd ? (double)V[(size_t)dead_c[d] * ldw + r] : 0.0;
-      for (int j = 0; j < nl; ++j) {
-        const double u = (double)V[(size_t)live_c[j] * ldw + r];
-#pragma unroll
-        for (int d = 0; d < SUB_MAX_DEAD; ++d) v[d] -= coef[j * SUB_MAX_DEAD + d] * u;
-      }
-#pragma unroll
-      for (int d = 0; d < SUB_MAX_DEAD; ++d)
-        if (d < nd) V[(size_t)dead_c[d] * ldw + r] = (float)v[d];
-    }
-    __syncthreads();
+    hipLaunchKernelGGL(sub_dots_kernel, dim3(m, 2), dim3(SUB_DT), 0, st, sd, sub, 0, L, ldw);
+    hipLaunchKernelGGL(sub_update_kernel, rows, dim3(SUB_RT), 0, st, sd, sub, L, ldw);
   }
-  // Gram matrix of the dead columns (row i: dots against every dead column; the lower
-  // triangle is used), then Cholesky on one wave
-  for (int i = wave; i < nd; i += NWAVE) dots_vs_dead(V + (size_t)dead_c[i] * ldw, gl + i * SUB_MAX_DEAD);
-  __syncthreads();
-  if (tid < WAVE) {
-    for (int j = 0; j < nd; ++j) {
-      double sjj = gl[j * SUB_MAX_DEAD + j];
-      for (int k = 0; k < j; ++k) sjj -= gl[j * SUB_MAX_DEAD + k] * gl[j * SUB_MAX_DEAD + k];
-      // the columns had unit norm before the projections: a pivot this small means the column
-      // lies in the span of the others
-      const double ljj = sjj > 1e-8 ? sqrt(sjj) : 0.0;
-      for (int i = j + 1 + tid; i < nd; i += WAVE) {
-        double sij = gl[i * SUB_MAX_DEAD + j];
-        for (int k = 0; k < j; ++k) sij -= gl[i * SUB_MAX_DEAD + k] * gl[j * SUB_MAX_DEAD + k];
-        gl[i * SUB_MAX_DEAD + j] = ljj > 0.0 ? sij / ljj : 0.0;
-      }
-      if (tid == 0) gl[j * SUB_MAX_DEAD + j] = ljj;
-      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    }
-    // column c of L^-1 by forward substitution (lane c); a zero pivot zeroes its row
-    if (tid < nd) {
-      const int c = tid;
-      for (int i = 0; i < nd; ++i) {
-        double x = 0.0;
-        if (i >= c) {
-          x = i == c ? 1.0 : 0.0;
-          for (int k = c; k < i; ++k) x -= gl[i * SUB_MAX_DEAD + k] * li[k * SUB_MAX_DEAD + c];
-          const double lii = gl[i * SUB_MAX_DEAD + i];
-          x = lii > 0.0 ? x / lii : 0.0;
-        }
-        li[i * SUB_MAX_DEAD + c] = x;
-      }
-    }
-  }
-  __syncthreads();
-  // rows of the dead block times L^-T
-  // (every load of a row before any store, so the loads of a row go out together)
-  for (int r = tid; r < L; r += SUB_CT) {
-    double v[SUB_MAX_DEAD];
-#pragma unroll
-    for (int d = 0; d < SUB_MAX_DEAD; ++d) v[d] = d < nd ? (double)V[(size_t)dead_c[d] * ldw + r] : 0.0;
-    for (int d = 0; d < nd; ++d) {
-      double y = 0.0;
-#pragma unroll
-      for (int k = 0; k < SUB_MAX_DEAD; ++k)  // (constant k: v stays in registers)
-        if (k <= d) y += li[d * SUB_MAX_DEAD + k] * v[k];
-      V[(size_t)dead_c[d] * ldw + r] = (float)y;
-    }
-  }
+  hipLaunchKernelGGL(sub_dots_kernel, dim3(SUB_MAX_DEAD < m ? SUB_MAX_DEAD : m, 2), dim3(SUB_DT), 0, st, sd, sub, 1,
+                     L, ldw);
+  hipLaunchKernelGGL(sub_chol_kernel, dim3(2), dim3(WAVE), 0, st, sub);
+  hipLaunchKernelGGL(sub_transform_kernel, rows, dim3(SUB_RT), 0, st, sd, sub, L, ldw);
+  return hipGetLastError();
 }
 
 hipError_t run_eig_subspace(const double* SX, const double* SG, double inv_nx, double inv_ng, int L, int m,
                             int iters, int max_sweeps, bool warm, void* work, const EigOut& out,
                             int host_flags[EIG_HOST_FLAGS], hipStream_t st, bool wait) {
-  // (sub_complete_kernel sorts at most 128 columns into its shared lists)
-  if (L > JAC_MAX_LDW || m < 16 || m % 16 || m >= L || m > 128 || iters < 1) return hipErrorInvalidValue;
+  // (the completion's column lists hold at most SUB_MAX_COLS columns)
+  if (L > JAC_MAX_LDW || m < 16 || m % 16 || m >= L || m > SUB_MAX_COLS || iters < 1) return hipErrorInvalidValue;
   const EigLayout e = eig_layout(L);
   const EigBufs b = eig_bufs(work, e);
   int* flags = b.flags;
@@ -1293,7 +1373,7 @@ hipError_t run_eig_subspace(const double* SX, const double* SG, double inv_nx, d
   ja.nb = nb;
   ja.nc = m;
   // Columns under the noise floor are not rotated (their near-degenerate directions would
-  // keep the tournament busy for nothing); sub_complete_kernel makes them orthonormal to the
+  // keep the tournament busy for nothing); the completion kernels make them orthonormal to the
   // rest afterwards, so the next step's basis is orthonormal.
   ja.noise_rel = NOISE_REL;
   ja.max_sweeps = max_sweeps;
@@ -1316,8 +1396,8 @@ hipError_t run_eig_subspace(const double* SX, const double* SG, double inv_nx, d
     err = hipLaunchCooperativeKernel((const void*)jacobi_kernel, dim3(nb), dim3(JT), kargs, dyn, st);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(sub_normalize_kernel, dim3(m, 2), dim3(256), 0, st, sd, scale, b.res[0], b.res[1], e.ldw);
-    hipLaunchKernelGGL(sub_complete_kernel, dim3(2), dim3(SUB_CT), 0, st, sd, scale, m, L, e.ldw);
     if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = launch_sub_complete(sd, scale, b.sub, m, L, e.ldw, st)) != hipSuccess) return err;
   }
 
   TruncArgs ta;
