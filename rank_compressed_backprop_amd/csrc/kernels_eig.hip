@@ -1138,20 +1138,30 @@ __global__ __launch_bounds__(256) void sub_normalize_kernel(EigSides a, const do
 // compute units in five short kernels: lists, dots (one block per column), row updates and
 // the row transform (blocks of rows), and the factorisation (one wave per side).
 
-// Column lists from the norms the Jacobi left: live columns in index order, then dead ones.
-__global__ void sub_lists_kernel(EigSides a, const double* __restrict__ scale, int m, SubScratch* __restrict__ sub) {
-  const int side = blockIdx.x;
-  if (threadIdx.x != 0) return;
+// Column lists from the norms the Jacobi left: live columns in index order, then dead ones
+// (one wave per side; a ballot gives each column its place).
+__global__ __launch_bounds__(WAVE) void sub_lists_kernel(EigSides a, const double* __restrict__ scale, int m,
+                                                         SubScratch* __restrict__ sub) {
+  const int side = blockIdx.x, lane = threadIdx.x;
   SubScratch& S = sub[side];
   const double floor_g = NOISE_REL * scale[side];
+  const unsigned long long below = (1ull << lane) - 1ull;
   int nl = 0, nd = 0;
-  for (int c = 0; c < m; ++c) {
-    const double sg = (double)a.nrm[side][c];
-    if (sg * sg > floor_g) S.live[nl++] = c;
-    else S.dead[nd++] = c;
+  for (int c0 = 0; c0 < m; c0 += WAVE) {
+    const int c = c0 + lane;
+    const bool in = c < m;
+    const double sg = in ? (double)a.nrm[side][c] : 0.0;
+    const bool live = in && sg * sg > floor_g;
+    const unsigned long long lm = __ballot(live), dm = __ballot(in && !live);
+    if (live) S.live[nl + __popcll(lm & below)] = c;
+    else if (in) S.dead[nd + __popcll(dm & below)] = c;
+    nl += __popcll(lm);
+    nd += __popcll(dm);
   }
-  S.nl = nl;
-  S.nd_all = nd;
+  if (lane == 0) {
+    S.nl = nl;
+    S.nd_all = nd;
+  }
 }
 
 // Dots of one column against every completed dead column: block j takes live column j
@@ -1233,46 +1243,66 @@ __global__ __launch_bounds__(SUB_RT) void sub_update_kernel(EigSides a, SubScrat
     if (d < nd) V[(size_t)S.dead[d] * ldw + r] = (float)v[d];
 }
 
-// Cholesky factor of the dead columns' Gram matrix and its inverse, one wave per side.
+// Cholesky factor of the dead columns' Gram matrix and its inverse, one wave per side. Lane
+// i holds row i of the factor, lane c column c of the inverse; the entries they need from
+// other lanes are broadcast across the wave. Every entry is formed by the same subtractions
+// in the same order as the left-looking factorisation and the forward substitution.
+__device__ inline double lane_value(double v, int lane) {  // v of one lane (a uniform index), to every lane
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), lane);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), lane);
+  return __hiloint2double(hi, lo);
+}
+
 __global__ __launch_bounds__(WAVE) void sub_chol_kernel(SubScratch* __restrict__ sub) {
   SubScratch& S = sub[blockIdx.x];
   const int nd = S.nd_all < SUB_MAX_DEAD ? S.nd_all : SUB_MAX_DEAD;
   if (nd == 0) return;
-  __shared__ double gl[SUB_MAX_DEAD * SUB_MAX_DEAD];
-  __shared__ double li[SUB_MAX_DEAD * SUB_MAX_DEAD];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < nd * SUB_MAX_DEAD; e += WAVE) gl[e] = S.gram[e];
-  __syncthreads();
-  for (int j = 0; j < nd; ++j) {
-    double sjj = gl[j * SUB_MAX_DEAD + j];
-    for (int k = 0; k < j; ++k) sjj -= gl[j * SUB_MAX_DEAD + k] * gl[j * SUB_MAX_DEAD + k];
-    // the columns had unit norm before the projections: a pivot this small means the column
-    // lies in the span of the others
-    const double ljj = sjj > 1e-8 ? sqrt(sjj) : 0.0;
-    for (int i = j + 1 + tid; i < nd; i += WAVE) {
-      double sij = gl[i * SUB_MAX_DEAD + j];
-      for (int k = 0; k < j; ++k) sij -= gl[i * SUB_MAX_DEAD + k] * gl[j * SUB_MAX_DEAD + k];
-      gl[i * SUB_MAX_DEAD + j] = ljj > 0.0 ? sij / ljj : 0.0;
-    }
-    if (tid == 0) gl[j * SUB_MAX_DEAD + j] = ljj;
-    __syncthreads();
-  }
-  // column c of L^-1 by forward substitution (lane c); a zero pivot zeroes its row
-  if (tid < nd) {
-    const int c = tid;
-    for (int i = 0; i < nd; ++i) {
-      double x = 0.0;
-      if (i >= c) {
-        x = i == c ? 1.0 : 0.0;
-        for (int k = c; k < i; ++k) x -= gl[i * SUB_MAX_DEAD + k] * li[k * SUB_MAX_DEAD + c];
-        const double lii = gl[i * SUB_MAX_DEAD + i];
-        x = lii > 0.0 ? x / lii : 0.0;
+  const int i = threadIdx.x;
+  double l[SUB_MAX_DEAD];  // row i of the Gram matrix, then of its lower Cholesky factor
+#pragma unroll
+  for (int k = 0; k < SUB_MAX_DEAD; ++k) l[k] = (i < nd && k <= i) ? S.gram[i * SUB_MAX_DEAD + k] : 0.0;
+#pragma unroll
+  for (int j = 0; j < SUB_MAX_DEAD; ++j) {
+    if (j < nd) {
+      // the columns had unit norm before the projections: a pivot this small means the
+      // column lies in the span of the others, and its column of the factor is zero
+      const double sjj = lane_value(l[j], j);
+      const double ljj = sjj > 1e-8 ? sqrt(sjj) : 0.0;
+      if (i == j) l[j] = ljj;
+      else if (i > j) l[j] = ljj > 0.0 ? l[j] / ljj : 0.0;
+#pragma unroll
+      for (int k = 0; k < SUB_MAX_DEAD; ++k) {
+        if (k > j && k < nd) {
+          const double lkj = lane_value(l[j], k);
+          if (i >= k) l[k] -= l[j] * lkj;
+        }
       }
-      li[i * SUB_MAX_DEAD + c] = x;
     }
   }
-  __syncthreads();
-  for (int e = tid; e < nd * SUB_MAX_DEAD; e += WAVE) S.li[e] = li[e];
+  // column c of L^-1 (lane c) by forward substitution, row l_i broadcast from lane i; a zero
+  // pivot zeroes its row
+  const int c = i;
+  double x[SUB_MAX_DEAD];
+#pragma unroll
+  for (int r = 0; r < SUB_MAX_DEAD; ++r) {
+    x[r] = 0.0;
+    if (r < nd) {
+      double v = r == c ? 1.0 : 0.0;
+#pragma unroll
+      for (int k = 0; k < SUB_MAX_DEAD; ++k) {
+        if (k < r) {
+          const double lrk = lane_value(l[k], r);
+          if (k >= c) v -= lrk * x[k];
+        }
+      }
+      const double lrr = lane_value(l[r], r);
+      if (r >= c) x[r] = lrr > 0.0 ? v / lrr : 0.0;
+    }
+  }
+  if (c < nd)
+#pragma unroll
+    for (int r = 0; r < SUB_MAX_DEAD; ++r)
+      if (r < nd) S.li[r * SUB_MAX_DEAD + c] = x[r];
 }
 
 // Rows of the completed dead block times L^-T (every load of a row before any store), and
