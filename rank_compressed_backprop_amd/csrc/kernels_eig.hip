@@ -40,9 +40,12 @@ constexpr long SPIN_LIMIT = 1L << 24;  // ~1 s of polling before a wait gives up
 struct EigLayout {
   int ldw, nb, ncols;
   size_t wbytes, vbytes, nrmbytes, verbytes, colbytes;
+  size_t wnbytes;  // subspace solver: staging of C V, SUB_MAX_COLS columns
 };
 
 static size_t al256(size_t n) { return (n + 255) / 256 * 256; }
+
+constexpr int SUB_MAX_COLS = 128;  // widest basis the subspace solver takes
 
 static EigLayout eig_layout(int L) {
   EigLayout e;
@@ -57,6 +60,7 @@ static EigLayout eig_layout(int L) {
   e.nrmbytes = al256((size_t)L * sizeof(float));
   e.verbytes = al256((size_t)2 * nb * sizeof(int));
   e.colbytes = al256((size_t)e.ncols * sizeof(int));
+  e.wnbytes = al256((size_t)SUB_MAX_COLS * e.ldw * sizeof(float));
   return e;
 }
 
@@ -73,6 +77,7 @@ constexpr int F_BARRIER2 = 20;  // Gram check arrivals
 constexpr int F_INFO = 24;      // [2][INFO_WORDS] copy of each side's info block
 constexpr int F_GMAX = 40;      // [3 slots][2 sides] Gram check maxima (float bits)
 constexpr int F_EEXACT = 48;    // 2 doubles: ||C||_F^2 per side from the statistic (subspace solver)
+constexpr int F_SUBDONE = 52;   // subspace solver: the basis has converged, later steps do nothing
 constexpr size_t EIG_FLAGS_BYTES = 256;
 
 struct EigBufs {
@@ -87,13 +92,13 @@ struct EigBufs {
   float* res[2];    // subspace solver: Ritz residual ||C v_c - sigma_c v_c|| per column
   double* frob;     // subspace solver: per-block sums of ||C||_F^2 [2][SUB_FROB_BLOCKS]
   struct SubScratch* sub;  // subspace solver: basis completion, one per side
+  float* Wn[2];            // subspace solver: C V of a step, copied to W unless the basis has converged
 };
 constexpr size_t EIG_FROB_BYTES = 2 * 64 * sizeof(double);  // [2][SUB_FROB_BLOCKS]
 
 // Basis completion of the subspace solver (per side): the column lists, the Gram-Schmidt
 // coefficients of the live columns against the completed (dead) ones, the dead columns'
 // Gram matrix and the inverse of its Cholesky factor.
-constexpr int SUB_MAX_COLS = 128;  // widest basis the subspace solver takes
 constexpr int SUB_MAX_DEAD = 32;   // near-null basis columns completed per side and step (the rest are zeroed)
 struct SubScratch {
   double coef[SUB_MAX_COLS * SUB_MAX_DEAD];  // [live j][dead d]
@@ -142,13 +147,17 @@ static EigBufs eig_bufs(void* work, const EigLayout& e) {
   b.frob = (double*)p;
   p += EIG_FROB_BYTES;
   b.sub = (SubScratch*)p;  // EIG_SUB_BYTES: two of them, 256-byte aligned
+  p += EIG_SUB_BYTES;
+  b.Wn[0] = (float*)p;
+  p += e.wnbytes;
+  b.Wn[1] = (float*)p;
   return b;
 }
 
 size_t eig_workspace_bytes(int L) {
   const EigLayout e = eig_layout(L);
   return 6 * e.wbytes + 2 * e.vbytes + 4 * e.nrmbytes + EIG_FLAGS_BYTES + e.verbytes + 2 * e.colbytes +
-         EIG_FROB_BYTES + EIG_SUB_BYTES;
+         EIG_FROB_BYTES + EIG_SUB_BYTES + 2 * e.wnbytes;
 }
 
 // ---------------------------------------------------------------------------- set-up kernels
@@ -163,7 +172,10 @@ struct EigSides {
   float* V32[2];
   float* nrm[2];
   int* cols[2];
+  const int* skip;     // subspace solver: when *skip is set the step's kernels return at once (else null)
 };
+
+__device__ inline bool skipped(const int* skip) { return skip != nullptr && *skip != 0; }
 
 // W[c][r] = S[min(r,c)][max(r,c)] * inv_n (column-major, zero padding); flags non-finite sums.
 // For a warm start it also rounds column c of the accumulated rotation to float32 (V32):
@@ -197,6 +209,7 @@ __global__ __launch_bounds__(256) void identity_kernel(EigSides a, int ldw) {
 
 // Column norms of W: sigma_c = ||W[:, c]||, c < L.
 __global__ __launch_bounds__(64) void colnorm_kernel(EigSides a, int ldw, int L) {
+  if (skipped(a.skip)) return;
   const int c = blockIdx.x;
   const float* W = a.W[blockIdx.y];
   const int lane = threadIdx.x;
@@ -215,6 +228,7 @@ __global__ __launch_bounds__(64) void colnorm_kernel(EigSides a, int ldw, int L)
 // counts the first group. One block of 1024 threads per side (blockIdx.x), ncols <= 2048.
 __global__ __launch_bounds__(1024) void frob_alive_kernel(EigSides a, double* __restrict__ scale_out, int L,
                                                           int ncols, int* __restrict__ n_alive_out, double noise_rel) {
+  if (skipped(a.skip)) return;
   __shared__ int flag[2048];
   __shared__ int sum[1024];
   __shared__ double fro[1024];
@@ -288,6 +302,7 @@ struct JacobiArgs {
   int* barrier2;        // the Gram check's barrier
   unsigned* gmax;       // [3][2] Gram check maxima (float bits)
   int* abort;
+  const int* skip;      // subspace solver: set once the basis has converged (the launch returns at once), else null
   int* version;         // [2][nb]
   const int* cols[2];   // column order per side (alive columns first)
   const int* n_alive;   // [2]
@@ -589,6 +604,7 @@ __device__ inline void upper_tile_ij(int idx, int T, int& ti, int& tj) {
 // decisions. The maxima rotate over three slots: slot (s+1) mod 3 is cleared during
 // sweep s, after every block has read it at the end of sweep s-2.
 __global__ __launch_bounds__(JT) void jacobi_kernel(JacobiArgs a) {
+  if (skipped(a.skip)) return;  // the same for every block: none waits on another
   __shared__ JacobiSmem sm;
   extern __shared__ float Ydyn[];  // the pair's 16 columns, 16 * ldw floats
   const int nbmax = a.nb;
@@ -921,6 +937,7 @@ hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv
   hipError_t err;
   if ((err = launch_zero(flags, EIG_FLAGS_BYTES + e.verbytes, st)) != hipSuccess) return err;
   EigSides sd;
+  sd.skip = nullptr;
   sd.S[0] = SX;
   sd.S[1] = SG;
   sd.inv[0] = inv_nx;
@@ -964,6 +981,7 @@ hipError_t run_eig(const double* SX, const double* SG, double inv_nx, double inv
   ja.barrier2 = flags + F_BARRIER2;
   ja.gmax = (unsigned*)(flags + F_GMAX);
   ja.abort = flags + F_ABORT;
+  ja.skip = nullptr;
   ja.version = b.version;
   ja.cols[0] = b.cols[0];
   ja.cols[1] = b.cols[1];
@@ -1093,6 +1111,7 @@ __global__ __launch_bounds__(256) void seed_basis_kernel(EigSides a, int L, int 
 // the host sees it); copy the basis to the float64 matrix the Jacobi rotates along with W.
 __global__ __launch_bounds__(256) void sub_reset_kernel(EigSides a, int* __restrict__ flags, int* __restrict__ version,
                                                         int nver, int ldw) {
+  if (skipped(a.skip)) return;
   const int c = blockIdx.x, s = blockIdx.y;
   if (c == 0 && s == 0) {
     for (int i = threadIdx.x; i < F_INFO; i += 256)
@@ -1108,6 +1127,7 @@ __global__ __launch_bounds__(256) void sub_reset_kernel(EigSides a, int* __restr
 // column stays as it was, for the completion kernels to make orthogonal to the new one.
 __global__ __launch_bounds__(256) void sub_normalize_kernel(EigSides a, const double* __restrict__ scale, float* res0,
                                                             float* res1, int ldw) {
+  if (skipped(a.skip)) return;
   __shared__ double part[256];
   const int c = blockIdx.x, s = blockIdx.y;
   const float sig = a.nrm[s][c];
@@ -1142,6 +1162,7 @@ __global__ __launch_bounds__(256) void sub_normalize_kernel(EigSides a, const do
 // (one wave per side; a ballot gives each column its place).
 __global__ __launch_bounds__(WAVE) void sub_lists_kernel(EigSides a, const double* __restrict__ scale, int m,
                                                          SubScratch* __restrict__ sub) {
+  if (skipped(a.skip)) return;
   const int side = blockIdx.x, lane = threadIdx.x;
   SubScratch& S = sub[side];
   const double floor_g = NOISE_REL * scale[side];
@@ -1170,6 +1191,7 @@ __global__ __launch_bounds__(WAVE) void sub_lists_kernel(EigSides a, const doubl
 constexpr int SUB_DT = 256;
 __global__ __launch_bounds__(SUB_DT) void sub_dots_kernel(EigSides a, SubScratch* __restrict__ sub, int gram, int L,
                                                           int ldw) {
+  if (skipped(a.skip)) return;
   const int side = blockIdx.y, j = blockIdx.x;
   SubScratch& S = sub[side];
   const int nd = S.nd_all < SUB_MAX_DEAD ? S.nd_all : SUB_MAX_DEAD;
@@ -1212,6 +1234,7 @@ __global__ __launch_bounds__(SUB_DT) void sub_dots_kernel(EigSides a, SubScratch
 // in order, eight loads at a time.
 constexpr int SUB_RT = 256;
 __global__ __launch_bounds__(SUB_RT) void sub_update_kernel(EigSides a, SubScratch* __restrict__ sub, int L, int ldw) {
+  if (skipped(a.skip)) return;
   const int side = blockIdx.y;
   SubScratch& S = sub[side];
   const int nd = S.nd_all < SUB_MAX_DEAD ? S.nd_all : SUB_MAX_DEAD;
@@ -1253,7 +1276,8 @@ __device__ inline double lane_value(double v, int lane) {  // v of one lane (a u
   return __hiloint2double(hi, lo);
 }
 
-__global__ __launch_bounds__(WAVE) void sub_chol_kernel(SubScratch* __restrict__ sub) {
+__global__ __launch_bounds__(WAVE) void sub_chol_kernel(SubScratch* __restrict__ sub, const int* __restrict__ skip) {
+  if (skipped(skip)) return;
   SubScratch& S = sub[blockIdx.x];
   const int nd = S.nd_all < SUB_MAX_DEAD ? S.nd_all : SUB_MAX_DEAD;
   if (nd == 0) return;
@@ -1309,6 +1333,7 @@ __global__ __launch_bounds__(WAVE) void sub_chol_kernel(SubScratch* __restrict__
 // the dead columns beyond SUB_MAX_DEAD set to zero.
 __global__ __launch_bounds__(SUB_RT) void sub_transform_kernel(EigSides a, SubScratch* __restrict__ sub, int L,
                                                                int ldw) {
+  if (skipped(a.skip)) return;
   const int side = blockIdx.y;
   SubScratch& S = sub[side];
   const int nd_all = S.nd_all;
@@ -1333,6 +1358,46 @@ __global__ __launch_bounds__(SUB_RT) void sub_transform_kernel(EigSides a, SubSc
   }
 }
 
+// W <- C V of this step, unless the basis has already converged (then W, the norms and the
+// residuals of the converged step stay as they are for the truncation).
+__global__ __launch_bounds__(256) void sub_commit_kernel(EigSides a, float* Wn0, float* Wn1, int ldw) {
+  if (skipped(a.skip)) return;
+  const int c = blockIdx.x, s = blockIdx.y;
+  const float* __restrict__ src = (s ? Wn1 : Wn0) + (size_t)c * ldw;
+  float* __restrict__ dst = a.W[s] + (size_t)c * ldw;
+  for (int r = threadIdx.x; r < ldw; r += 256) dst[r] = src[r];
+}
+
+// After a step: the basis has converged when, on both sides, every column among the R_max
+// largest has a Ritz residual within tol * sigma_0 (the truncation keeps at most R_max of
+// them and applies the same test to those it keeps). Later steps then do nothing.
+__global__ __launch_bounds__(SUB_MAX_COLS) void sub_check_kernel(EigSides a, const float* __restrict__ res0,
+                                                                 const float* __restrict__ res1, int m, int R_max,
+                                                                 float tol, int* __restrict__ done) {
+  if (*done) return;
+  __shared__ int fail;
+  if (threadIdx.x == 0) fail = 0;
+  __syncthreads();
+  const int c = threadIdx.x;
+  for (int side = 0; side < 2; ++side) {
+    const float* __restrict__ nrm = a.nrm[side];
+    const float* __restrict__ res = side ? res1 : res0;
+    if (c < m) {
+      float sig0 = 0.0f;
+      int rank = 0;
+      const float sc = nrm[c];
+      for (int k = 0; k < m; ++k) {
+        const float sk = nrm[k];
+        sig0 = fmaxf(sig0, sk);
+        rank += (sk > sc) || (sk == sc && k < c);
+      }
+      if (rank < R_max && !(res[c] <= tol * sig0)) fail = 1;  // (a NaN residual fails too)
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && !fail) *done = 1;
+}
+
 static hipError_t launch_sub_complete(const EigSides& sd, const double* scale, SubScratch* sub, int m, int L, int ldw,
                                       hipStream_t st) {
   const dim3 rows((L + SUB_RT - 1) / SUB_RT, 2);
@@ -1343,7 +1408,7 @@ static hipError_t launch_sub_complete(const EigSides& sd, const double* scale, S
   }
   hipLaunchKernelGGL(sub_dots_kernel, dim3(SUB_MAX_DEAD < m ? SUB_MAX_DEAD : m, 2), dim3(SUB_DT), 0, st, sd, sub, 1,
                      L, ldw);
-  hipLaunchKernelGGL(sub_chol_kernel, dim3(2), dim3(WAVE), 0, st, sub);
+  hipLaunchKernelGGL(sub_chol_kernel, dim3(2), dim3(WAVE), 0, st, sub, sd.skip);
   hipLaunchKernelGGL(sub_transform_kernel, rows, dim3(SUB_RT), 0, st, sd, sub, L, ldw);
   return hipGetLastError();
 }
@@ -1361,6 +1426,7 @@ hipError_t run_eig_subspace(const double* SX, const double* SG, double inv_nx, d
   hipError_t err;
   if ((err = launch_zero(flags, EIG_FLAGS_BYTES + e.verbytes, st)) != hipSuccess) return err;
   EigSides sd;
+  sd.skip = flags + F_SUBDONE;
   sd.S[0] = SX;
   sd.S[1] = SG;
   sd.inv[0] = inv_nx;
@@ -1394,6 +1460,7 @@ hipError_t run_eig_subspace(const double* SX, const double* SG, double inv_nx, d
   ja.barrier2 = flags + F_BARRIER2;
   ja.gmax = (unsigned*)(flags + F_GMAX);
   ja.abort = flags + F_ABORT;
+  ja.skip = flags + F_SUBDONE;
   ja.version = b.version;
   ja.cols[0] = b.cols[0];
   ja.cols[1] = b.cols[1];
@@ -1416,9 +1483,10 @@ hipError_t run_eig_subspace(const double* SX, const double* SG, double inv_nx, d
     if ((err = hipGetLastError()) != hipSuccess) return err;
     // W[c][r] = sum_k V[k][c] C[k][r]: A = V^T [m][ldw] (k contiguous), B = C [k][r]
     if ((err = launch_gemm(false, false, b.V32[0], e.ldw, (size_t)(b.V32[1] - b.V32[0]), b.Wtmp[0], e.ldw,
-                           (size_t)(b.Wtmp[1] - b.Wtmp[0]), b.W[0], e.ldw, (size_t)(b.W[1] - b.W[0]), 2, m, e.ldw,
+                           (size_t)(b.Wtmp[1] - b.Wtmp[0]), b.Wn[0], e.ldw, (size_t)(b.Wn[1] - b.Wn[0]), 2, m, e.ldw,
                            L, st)) != hipSuccess)
       return err;
+    hipLaunchKernelGGL(sub_commit_kernel, dim3(m, 2), dim3(256), 0, st, sd, b.Wn[0], b.Wn[1], e.ldw);
     hipLaunchKernelGGL(colnorm_kernel, dim3(m, 2), dim3(64), 0, st, sd, e.ldw, L);
     hipLaunchKernelGGL(frob_alive_kernel, dim3(2), dim3(1024), 0, st, sd, scale, m, m, flags + F_NALIVE,
                        NOISE_REL);
@@ -1428,6 +1496,9 @@ hipError_t run_eig_subspace(const double* SX, const double* SG, double inv_nx, d
     hipLaunchKernelGGL(sub_normalize_kernel, dim3(m, 2), dim3(256), 0, st, sd, scale, b.res[0], b.res[1], e.ldw);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = launch_sub_complete(sd, scale, b.sub, m, L, e.ldw, st)) != hipSuccess) return err;
+    if (it + 1 < iters)
+      hipLaunchKernelGGL(sub_check_kernel, dim3(1), dim3(SUB_MAX_COLS), 0, st, sd, b.res[0], b.res[1], m,
+                         out.R_max, SUB_RES_TOL, flags + F_SUBDONE);
   }
 
   TruncArgs ta;
