@@ -79,10 +79,11 @@ typedef enum { INSTANT_COMP_PAPER = 0, INSTANT_COMP_NONE = 1, INSTANT_COMP_RATIO
  * and E = sum_i sigma_i^2 = ||C||_F^2 are needed).
  *   JACOBI    the full decomposition: blocked one-sided Jacobi on all L columns, warm
  *             started from the previous finalize's rotation.
- *   SUBSPACE  the top m = R_max + 16 (rounded up to 16) eigenpairs by sub_iters steps of
- *             block subspace iteration with Rayleigh-Ritz (W = C V on the matrix cores,
- *             one-sided Jacobi on the m columns), warm started from the previous
- *             finalize's basis; E is taken from C. Status E_RANK when eps * E lies beyond
+ *   SUBSPACE  the top m = R_max + 16 (rounded up to 16) eigenpairs by at most sub_iters
+ *             steps of block subspace iteration with Rayleigh-Ritz (W = C V on the matrix
+ *             cores, one-sided Jacobi on the m columns), warm started from the previous
+ *             finalize's basis, stopping after the first step whose R_max largest Ritz
+ *             pairs all pass the residual test below; E is taken from C. Status E_RANK when eps * E lies beyond
  *             the m directions, E_NOCONV when a kept direction's Ritz residual exceeds
  *             3e-5 * sigma_0. When m >= L it is the JACOBI solver. sigma_x / sigma_g
  *             then hold the m leading values followed by zeros. */
@@ -103,7 +104,7 @@ typedef struct {
   int32_t comp;       /* instant_comp */
   int32_t max_sweeps; /* Jacobi sweep limit (e.g. 30); per subspace step for SUBSPACE */
   int32_t solver;     /* instant_solver */
-  int32_t sub_iters;  /* subspace steps per finalize (SUBSPACE; >= 1) */
+  int32_t sub_iters;  /* most subspace steps per finalize (SUBSPACE; >= 1) */
 } instant_config;
 
 typedef struct {
