@@ -180,3 +180,32 @@ def test_subspace_too_few_steps_is_noconv_and_publishes_nothing():
     _, info = lay.query()
     print(f"[subspace] effformer/up 6 steps: {rcb.instant_status_str(s)}, generation {info.generation}", flush=True)
     assert info.generation == 0 and info.Rx == 0 and info.Ry == 0
+
+
+def test_subspace_stops_once_converged():
+    """A finalize stops after the first step whose R_max largest Ritz pairs pass the residual
+    test: with a step limit beyond that step the later steps do nothing, so limits of 6 and
+    40 publish bit-identical projections and sigma (cold window, then warm)."""
+    import rank_compressed_backprop_amd as rcb
+    wl = W.get_workload("bert_attn")
+    ly = wl.layer("main")
+    lays = [_layer(wl, ly, 64, sub_iters=6), _layer(wl, ly, 64, sub_iters=40)]
+    for window in range(2):
+        _feed(lays, wl, "main", range(window * wl.n_cal, (window + 1) * wl.n_cal))
+        got = []
+        for lay in lays:
+            s = lay.calibrate(None, None, 0, finalize=True)
+            assert s == rcb.INSTANT_OK, rcb.instant_status_str(s)
+            _, info = lay.query()
+            P = torch.empty((info.Rx, wl.L), device="cuda")
+            Q = torch.empty((info.Ry, wl.L), device="cuda")
+            sx = torch.empty(wl.L, device="cuda")
+            sg = torch.empty(wl.L, device="cuda")
+            lay.get_projections(P, Q, sx, sg)
+            torch.cuda.synchronize()
+            got.append((info, P, Q, sx, sg))
+        (i6, *t6), (i40, *t40) = got
+        print(f"[subspace] window {window}: k/R x {i6.kx}/{i6.Rx} g {i6.ky}/{i6.Ry} with limits 6 and 40", flush=True)
+        assert (i6.kx, i6.Rx, i6.ky, i6.Ry) == (i40.kx, i40.Rx, i40.ky, i40.Ry)
+        for a, b in zip(t6, t40):
+            assert torch.equal(a, b)
