@@ -76,10 +76,10 @@ def parse():
                     help="before the timed region, copy a buffer of this many MiB three times (a plain "
                          "copy kernel of known size that scales the profiler's byte counters)")
     ap.add_argument("--cpu-sample", type=int, default=8, help="samples of a batch the oracle times")
-    ap.add_argument("--solver", default="jacobi", choices=("jacobi", "subspace"),
-                    help="eigensolver of the finalize: the full Jacobi decomposition, or the top-m "
-                         "subspace iteration")
-    ap.add_argument("--sub-iters", type=int, default=6, help="subspace steps per finalize")
+    ap.add_argument("--solver", default="subspace", choices=("jacobi", "subspace"),
+                    help="eigensolver of the finalize: the top-m subspace iteration (stops once its "
+                         "Ritz residuals pass), or the full Jacobi decomposition")
+    ap.add_argument("--sub-iters", type=int, default=6, help="most subspace steps per finalize")
     ap.add_argument("--sync-finalize", action="store_true",
                     help="finalize synchronously (the host waits for the outcome) instead of queueing it "
                          "and letting the next forward compression after it pick up the new projections")
