@@ -134,6 +134,15 @@ def main():
     lay = rcb.InstantLayer(rcb.make_config(L, Cx, Cy, B, R_max=R_max, p=wl.p, N_t=wl.n_t, eps=wl.eps,
                                            dtype=wl.dtype, comp="paper", solver=args.solver,
                                            sub_iters=args.sub_iters), device=dev)
+    # the library takes the full decomposition when the subspace basis (R_max + 16 columns,
+    # rounded up to 16, R_max clamped to L) would not be narrower than L
+    m_sub = (min(R_max, L) + 16 + 15) // 16 * 16
+    if args.solver == "jacobi":
+        solver_used = "jacobi"
+    elif m_sub < L:
+        solver_used = f"subspace (at most {args.sub_iters} steps)"
+    else:
+        solver_used = f"jacobi (a subspace basis of {m_sub} columns is not narrower than L = {L})"
     xhat = torch.empty((B, R_max, Cx), dtype=tdt, device=dev)
     gw = torch.empty((Cy, Cx), dtype=tdt, device=dev)
     gx = torch.empty((B, L, Cx), dtype=tdt, device=dev)
@@ -292,7 +301,7 @@ def main():
                 100.0 * flops_acc / t_acc / 1e12 / (MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else
                                                     MFMA_FP32_PEAK_TFLOPS),
             "statistics_GBs": es * B * L * (Cx + Cy) / t_acc / 1e9,
-            "eigensolver": args.solver if args.solver == "jacobi" else f"subspace ({args.sub_iters} steps)",
+            "eigensolver": solver_used,
             "cold_finalize_ms": t_cold * 1e3,
             "finalize_ms": t_fin * 1e3,
             "finalize_in_loop_ms": (sum(fin_loop) / len(fin_loop) * 1e3) if fin_loop else None,
