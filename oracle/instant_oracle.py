@@ -25,6 +25,28 @@ Readings where the notes leave a step open (each one also listed in the design n
     "none" c = 1; "ratio" c = (E / sum_{i<=R} sigma_i^2)^(1/2). P = c * U_R^T.
   * eps is the float32 value the library receives, upcast: float64(float32(eps)).
   * g_y is projected by P for g_w and by Q for g_x ([KD3] equations).
+
+What pins each function to something other than itself (tests/pins.py; every check
+also catches a planted mistake in tests/test_oracle_mutations.py):
+  eps_as_f32               float32(0.95) = 15938355 / 2^24 written out, and two golden
+                           spectra whose k differs between float32(0.95) and 0.95
+  Accumulator,
+  autocorr_entries         element-wise loop definition; sampled entries vs the full sum
+  canonical_signs          hand-built columns with ties and a zero column (golden)
+  spectrum                 eigen invariants; closed-form Hadamard spectrum
+  truncate                 exact rational brute force on golden and random dyadic spectra
+  margin                   hand-computed golden margins; moving the threshold by less than
+                           the margin keeps k, by a little more changes it (brute force)
+  compensation,
+  build_projection         hand-built spectrum values; P P^T = c^2 I
+  calibrate_side,
+  calibrate                through C = H diag(lam) H^T; exact low-rank recovery
+  compress, backward       R = L identity (exact gradients); unreordered projector form
+                           with unrelated P and Q; product count against the FLOP formula
+  dense_projector_backward the same projector form written with einsum
+  exact_backward           element-wise loop definition of g_w and g_x
+  flops_*                  the 192/7 ratio of the BERT-block example ([KD3])
+No function is left unpinned.
 """
 from __future__ import annotations
 
@@ -36,7 +58,7 @@ __all__ = [
     "Accumulator", "autocorr_entries", "spectrum", "truncate", "compensation", "build_projection",
     "calibrate_side", "calibrate", "compress", "backward", "dense_projector_backward",
     "exact_backward", "flops_lowrank_formula", "flops_vanilla_formula", "FlopCounter",
-    "canonical_signs", "eps_as_f32",
+    "canonical_signs", "eps_as_f32", "margin",
 ]
 
 # status codes of the calibration (same meaning as the library's)

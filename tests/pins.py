@@ -313,10 +313,126 @@ def check_autocorr_entries(O, seed=12):
     assert np.abs(got - O.autocorr_entries([t1, t2], cols, rows)).max() == 0.0
 
 
+# --------------------------------------------------------------------------- eps as float32
+def check_eps_is_float32(O):
+    """The library receives eps as a float32; the oracle's threshold uses that value.
+    float32(0.95) = 15938355 / 2^24 (the nearest float32 to 0.95, below it); 0.625 is exact.
+    The golden spectra float32_eps_* (truncation_spectra.json) decide k differently under
+    float32(0.95) and 0.95, and the truncation through calibrate_side must take the
+    float32 branch too."""
+    assert Fraction(O.eps_as_f32(0.95)) == Fraction(15938355, 2 ** 24)
+    assert O.eps_as_f32(0.625) == 0.625
+    assert O.eps_as_f32(1.0) == 1.0
+    g = load_golden("truncation_spectra.json")
+    cases = [c for c in g["cases"] if c["name"].startswith("float32_eps")]
+    assert len(cases) == 2
+    for case in cases:
+        sigma = np.array(case["sigma"], dtype=np.float64)
+        # C = diag(sigma) is exact, and its decomposition returns sigma itself
+        s = O.calibrate_side(np.diag(sigma), case["eps"], case["p"], O.COMP_NONE, len(sigma))
+        assert s["status"] == O.OK and (s["k"], s["R"]) == (case["k"], case["R"]), (case["name"], s["k"])
+
+
+# --------------------------------------------------------------------------- margin of the k decision
+def check_margin_golden(O):
+    """Hand-computed margins (tests/golden/margin_cases.json)."""
+    g = load_golden("margin_cases.json")
+    for case in g["cases"]:
+        sigma = np.array(case["sigma"], dtype=np.float64)
+        st, k, R, prefix = O.truncate(sigma, case["eps"], 0)
+        assert st == O.OK and k == case["k"], (case["name"], k)
+        m = O.margin(prefix, k, case["eps"])
+        assert abs(m - case["margin"]) <= 1e-15, (case["name"], m, case["margin"])
+
+
+def check_margin_property(O, trials=300, seed=13):
+    """What the margin means: moving the threshold by less than margin * E in either
+    direction keeps k, and moving it by a little more towards the nearer deciding prefix
+    sum changes k. Brute force on random dyadic spectra (exact prefix sums)."""
+    rng = np.random.default_rng(seed)
+    for _ in range(trials):
+        L = int(rng.integers(2, 30))
+        sigma = np.sort(rng.integers(0, 9, size=L).astype(np.float64) / 4.0)[::-1].copy()
+        sigma[0] = max(sigma[0], 1.0)
+        eps = int(rng.integers(1, 64)) / 64.0 + 1.0 / 1024.0
+        st, k, _, prefix = O.truncate(sigma, eps, 0)
+        assert st == O.OK
+        m = O.margin(prefix, k, eps)
+        E = prefix[-1]
+        below = prefix[k - 2] if k >= 2 else 0.0
+        assert m > 0.0
+        for f in (0.99, -0.99):
+            e2 = eps + f * m
+            if 0.0 < e2 <= 1.0:
+                assert brute_force_k_f64(sigma, e2) == k, (sigma, eps, m, f)
+        # the nearer side: the prefix sum S_k (threshold moving up past it changes k to k+1)
+        # or S_{k-1} (threshold moving down past it changes k to k-1 or less)
+        up = abs(prefix[k - 1] - eps * E) <= abs(below - eps * E)
+        e2 = eps + (1.01 * m if up else -1.01 * m)
+        if 0.0 < e2 <= 1.0:
+            assert brute_force_k_f64(sigma, e2) != k, (sigma, eps, m)
+
+
+def brute_force_k_f64(sigma, eps):
+    """Smallest k with sum_{i<=k} sigma_i^2 >= eps * E, in exact rationals, eps taken as given."""
+    sq = [Fraction(float(s)) ** 2 for s in sigma]
+    thr = Fraction(float(eps)) * sum(sq)
+    run = Fraction(0)
+    for j, v in enumerate(sq):
+        run += v
+        if run >= thr:
+            return j + 1
+    raise AssertionError("unreachable")
+
+
+# --------------------------------------------------------------------------- exact gradients
+def check_exact_backward_loops(O, seed=14):
+    """The full-rank gradients of y = x w^T from their element-wise definition:
+    g_w[o][i] = sum_b sum_l gy[b][l][o] x[b][l][i] and g_x[b][l][i] = sum_o gy[b][l][o] w[o][i]
+    (plain Python loops; Cx != Cy so a transposed operand cannot pass)."""
+    rng = np.random.default_rng(seed)
+    B, L, Cx, Cy = 2, 3, 2, 4
+    x = rng.standard_normal((B, L, Cx))
+    gy = rng.standard_normal((B, L, Cy))
+    w = rng.standard_normal((Cy, Cx))
+    gw = [[0.0] * Cx for _ in range(Cy)]
+    for o in range(Cy):
+        for i in range(Cx):
+            for b in range(B):
+                for l in range(L):
+                    gw[o][i] += gy[b, l, o] * x[b, l, i]
+    gx = [[[0.0] * Cx for _ in range(L)] for _ in range(B)]
+    for b in range(B):
+        for l in range(L):
+            for i in range(Cx):
+                for o in range(Cy):
+                    gx[b][l][i] += gy[b, l, o] * w[o, i]
+    out = O.exact_backward(x, gy, w)
+    assert np.shape(out["gw"]) == (Cy, Cx) and np.shape(out["gx"]) == (B, L, Cx)
+    assert np.abs(np.asarray(out["gw"]) - np.array(gw)).max() < 1e-12
+    assert np.abs(np.asarray(out["gx"]) - np.array(gx)).max() < 1e-12
+
+
+# --------------------------------------------------------------------------- eigenvector gauge
+def check_canonical_signs_golden(O):
+    """Sign rule on hand-built columns with ties and a zero column
+    (tests/golden/canonical_signs.json)."""
+    g = load_golden("canonical_signs.json")
+    U = np.array(g["input_columns"], dtype=np.float64).T
+    want = np.array(g["expected_columns"], dtype=np.float64).T
+    got = O.canonical_signs(U)
+    assert np.array_equal(got, want), got
+    assert np.array_equal(U, np.array(g["input_columns"], dtype=np.float64).T)  # input untouched
+    # spectrum() returns its vectors in that gauge
+    _, V = O.spectrum(np.diag([3.0, 2.0, 1.0]) - 0.5 * np.ones((3, 3)))
+    assert np.array_equal(V, O.canonical_signs(V))
+
+
 ALL_CHECKS = [
     check_full_rank_identity, check_reordering, check_truncation_golden,
     check_truncation_bruteforce, check_truncation_through_matrix, check_error_semantics,
     check_flop_formula, check_eigen_invariants, check_exact_lowrank_recovery,
     check_compensation_algebra, check_monotone_in_p, check_memory_count, check_autocorrelation,
-    check_autocorr_entries,
+    check_autocorr_entries, check_eps_is_float32, check_margin_golden, check_margin_property,
+    check_exact_backward_loops, check_canonical_signs_golden,
 ]

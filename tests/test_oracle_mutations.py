@@ -105,11 +105,75 @@ def _lowrank_formula_wrong(L, Cx, Cy, Rx, Ry):
     return 2 * (Rx + Ry) * (Cx * Cy + L * Cx)
 
 
+def _eps_unrounded(eps):
+    # the decimal threshold instead of the float32 value the library receives
+    return float(eps)
+
+
+def _margin_shift_up(prefix, k, eps):
+    # reads S_{k+1} and S_k instead of S_k and S_{k-1}
+    E = prefix[-1]
+    thr = eps * E
+    nxt = prefix[k] if k < len(prefix) else prefix[-1]
+    return float(min(abs(nxt - thr), abs(prefix[k - 1] - thr)) / E)
+
+
+def _margin_shift_down(prefix, k, eps):
+    # reads S_{k-1} and S_{k-2} instead of S_k and S_{k-1}
+    E = prefix[-1]
+    thr = eps * E
+    a = prefix[k - 2] if k >= 2 else 0.0
+    b = prefix[k - 3] if k >= 3 else 0.0
+    return float(min(abs(a - thr), abs(b - thr)) / E)
+
+
+def _margin_absolute(prefix, k, eps):
+    # not relative to E
+    return _ORIG_MARGIN(prefix, k, eps) * prefix[-1]
+
+
+def _exact_gx_scaled(x, gy, w):
+    out = _ORIG_EXACT(x, gy, w)
+    out["gx"] = 1.5 * out["gx"]
+    return out
+
+
+def _exact_gw_first_sample(x, gy, w):
+    out = _ORIG_EXACT(x, gy, w)
+    out["gw"] = np.asarray(gy, dtype=np.float64)[0].T @ np.asarray(x, dtype=np.float64)[0]
+    return out
+
+
+def _signs_untouched(U):
+    return np.array(U, dtype=np.float64, copy=True)
+
+
+def _signs_tie_to_last(U):
+    # ties of the largest magnitude go to the highest index
+    U = np.array(U, dtype=np.float64, copy=True)
+    a = np.abs(U)[::-1]
+    idx = U.shape[0] - 1 - np.argmax(a, axis=0)
+    s = np.sign(U[idx, np.arange(U.shape[1])])
+    s[s == 0] = 1.0
+    return U * s[None, :]
+
+
+def _signs_largest_value(U):
+    # the largest signed value instead of the largest magnitude
+    U = np.array(U, dtype=np.float64, copy=True)
+    idx = np.argmax(U, axis=0)
+    s = np.sign(U[idx, np.arange(U.shape[1])])
+    s[s == 0] = 1.0
+    return U * s[None, :]
+
+
 _ORIG_TRUNCATE = M.truncate
 _ORIG_SPECTRUM = M.spectrum
 _ORIG_COMP = M.compensation
 _ORIG_BACKWARD = M.backward
 _ORIG_COMPRESS = M.compress
+_ORIG_MARGIN = M.margin
+_ORIG_EXACT = M.exact_backward
 
 MUTATIONS = [
     ("truncate", _truncate_strict),
@@ -127,6 +191,15 @@ MUTATIONS = [
     ("compress", _compress_reversed_tokens),
     ("Accumulator", _AccPerChannel),
     ("flops_lowrank_formula", _lowrank_formula_wrong),
+    ("eps_as_f32", _eps_unrounded),
+    ("margin", _margin_shift_up),
+    ("margin", _margin_shift_down),
+    ("margin", _margin_absolute),
+    ("exact_backward", _exact_gx_scaled),
+    ("exact_backward", _exact_gw_first_sample),
+    ("canonical_signs", _signs_untouched),
+    ("canonical_signs", _signs_tie_to_last),
+    ("canonical_signs", _signs_largest_value),
 ]
 
 
