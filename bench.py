@@ -6,14 +6,21 @@ statistics over N_cal=16 batches, recalibration every N_t=100 steps (shapes of t
 BERT layers the INSTANT notes evaluate; synthetic token-low-rank data, see
 workloads/).
 
-One step is one training step's share of the method on one batch, on the notes'
-schedule (section 整体框架): every step compresses x (x_hat = P x) and runs the
-low-rank backward (g_w, g_x); the first N_cal steps of every N_t-step window also
-accumulate the statistics, and the last of them finalizes (eigen-decomposition,
-truncation, new P and Q). So every kernel of the path runs inside the timed region,
-with the calibration amortised exactly as the schedule amortises it.
+The metric (`value`) is the low-rank backward's throughput: tokens/s = B * L / t_bwd,
+where t_bwd is the median time of one instant_backward (the stacked projection of g_y,
+g_w, g_hat_x and the expansion; notes section 关键设计 3). It is measured with HIP events
+on the launch stream around runs of 8 consecutive instant_backward calls, 200 timed runs
+after 20 untimed ones, each call on its own resident batch (g_y, x_hat, g_x rotate over
+the resident set, beyond the 256 MB last-level cache); p10 and p90 of the per-call time
+are reported beside it, and the same runs replayed from a HIP graph for comparison.
 
-Prints one JSON line; `value` is tokens/s = steps * B * L / wall time.
+The driver's `--steps K --warmup W` steps are whole passes of the path on the notes'
+schedule (section 整体框架): every step compresses x (x_hat = P x) and runs the low-rank
+backward; the first N_cal steps of every N_t-step window also accumulate the statistics,
+and the last of them finalizes (eigen-decomposition, truncation, new P and Q). Their wall
+time gives `ms_per_step`. Because K is usually less than a window, the schedule's own rate
+is measured separately over two whole N_t windows (`parts.schedule_*`), so it does not
+depend on K.
 """
 from __future__ import annotations
 
@@ -33,24 +40,29 @@ MFMA_FP32_PEAK_TFLOPS = 157.3   # MI355X dense fp32
 WORKLOAD_NAMES = {"tiny": "tiny fp32", "bert_attn": "BERT-base attention projection",
                   "bert_ffn": "BERT-base FFN", "effformer": "EfficientFormer-L1 last-stage",
                   "llm_mlp": "LLM MLP"}
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "proj_bert_attn_traffic.json")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "backward_bert_attn_traffic.json")
+CALLS_PER_RUN = 8
+TIMED_RUNS = 200
+WARM_RUNS = 20
 
 
-def measured_traffic():
-    """HBM bytes per forward-compression launch from the recorded rocprofv3 counters
-    (FETCH_SIZE and WRITE_SIZE scaled by a copy kernel of known size), or None when the
-    kernel sources changed since the counters were taken."""
+def measured_traffic(workload):
+    """HBM bytes per instant_backward from the recorded rocprofv3 counters (FETCH_SIZE and
+    WRITE_SIZE of the backward's kernels, scaled by a copy kernel of known size), or None
+    when the record is for another workload or the kernel sources changed since."""
     import hashlib
     try:
         with open(TRAFFIC_RECORD) as f:
             rec = json.load(f)
+        if rec.get("workload") != workload:
+            return None
         h = hashlib.sha256()
         for src in rec["sources"]:
             with open(os.path.join(ROOT, src), "rb") as f:
                 h.update(f.read())
         if h.hexdigest() != rec["sources_sha256"]:
             return None
-        return rec["traffic_bytes_per_launch"]
+        return rec["traffic_bytes_per_backward"]
     except (OSError, KeyError, ValueError):
         return None
 
@@ -58,17 +70,18 @@ def measured_traffic():
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=100, help="timed steps of the whole path (the driver's K)")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed steps before them")
     ap.add_argument("--workload", default="bert_attn",
                     help="bert_attn (the headline line); bert_block (every linear layer of a BERT-base "
                          "encoder layer: its low-rank backward against the exact one); or one layer of "
-                         "tiny, bert_ffn, effformer, llm_mlp run through the same step loop")
+                         "tiny, bert_ffn, effformer, llm_mlp run through the same measurement")
     ap.add_argument("--layer", default="0", help="layer of a two-layer workload (up or down)")
     ap.add_argument("--batches", type=int, default=None,
                     help="distinct resident batches cycled through (default 32: more than N_cal, so "
                          "consecutive calibration windows see different statistics; N_cal for llm_mlp, "
                          "whose batches take seconds each to generate)")
+    ap.add_argument("--windows", type=int, default=2, help="whole N_t windows timed for the schedule rate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--one-stream", action="store_true",
                     help="run the statistics on the main stream too (no overlap with the hot path)")
@@ -84,6 +97,16 @@ def parse():
                     help="finalize synchronously (the host waits for the outcome) instead of queueing it "
                          "and letting the next forward compression after it pick up the new projections")
     return ap.parse_args()
+
+
+def quantile(v, q):
+    v = sorted(v)
+    if not v:
+        return None
+    pos = q * (len(v) - 1)
+    lo = int(pos)
+    hi = min(lo + 1, len(v) - 1)
+    return v[lo] + (v[hi] - v[lo]) * (pos - lo)
 
 
 def main():
@@ -120,6 +143,8 @@ def main():
     # resident synthetic batches (distinct, so the 256 MB last-level cache cannot hold a step's data)
     nb = args.batches if args.batches is not None else (wl.n_cal if L * (Cx + Cy) * B > 1 << 27 else 32)
     nb = max(nb, wl.n_cal)
+    print(f"[bench] {wl.name}/{ly.name}: B={B} L={L} Cx={Cx} Cy={Cy} {wl.dtype}; generating {nb} resident "
+          "batches", file=sys.stderr, flush=True)
     xs, gys = [], []
     for t in range(nb):
         d = W.make_layer_batch(wl, li, t)
@@ -169,7 +194,7 @@ def main():
     # main one (the overlap the C ABI allows: they use disjoint parts of the workspace; the
     # resident inputs are ready on both streams). A finalizing call first waits for the
     # main stream's calls, since it rewrites the projection buffer they may still read.
-    # The finalizing calls inside the timed loop are bracketed by HIP events on the side
+    # The finalizing calls of the schedule windows are bracketed by HIP events on the side
     # stream (one pair per window; the span includes that step's statistics batch and the
     # host round trip of the finalize).
     finalize_mode = True if args.sync_finalize else "async"
@@ -197,31 +222,96 @@ def main():
                 raise RuntimeError("calibration failed: " + rcb.instant_status_str(s))
 
     side_st.wait_stream(main_st)  # the resident batches and the set-up's projections
+    # ---- the driver's steps: W untimed, then exactly K timed passes of the whole path
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # every successful finalize publishes one new generation of projections; an asynchronous
-    # one that fails is only seen here (the old projections stay in use)
-    gen0 = lay.query()[1].generation
     t0 = time.perf_counter()
     for i in range(args.warmup, args.warmup + args.steps):
-        step(i, timed=True)
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    print(f"[bench] {args.steps} timed steps of the whole path: {wall / args.steps * 1e3:.4f} ms a step",
+          file=sys.stderr, flush=True)
+
+    # ---- the schedule's rate over whole N_t windows (independent of K): from the next
+    # window boundary, `windows` full windows, statistics and finalize included
+    i0 = (args.warmup + args.steps + wl.n_t - 1) // wl.n_t * wl.n_t
+    for i in range(args.warmup + args.steps, i0):
+        step(i)
+    torch.cuda.synchronize()
+    gen0 = lay.query()[1].generation
+    fin_events.clear()
+    n_sched = args.windows * wl.n_t
+    ts0 = time.perf_counter()
+    for i in range(i0, i0 + n_sched):
+        step(i, timed=True)
+    torch.cuda.synchronize()
+    wall_sched = time.perf_counter() - ts0
     fin_loop = [a.elapsed_time(b) * 1e-3 for a, b in fin_events]
     _, info = lay.query()
     published = info.generation - gen0
     if published != len(fin_events):
-        print(f"warning: {len(fin_events) - published} of {len(fin_events)} finalizes in the timed loop "
+        print(f"warning: {len(fin_events) - published} of {len(fin_events)} finalizes in the schedule windows "
               "published no projections", file=sys.stderr)
     Rx, Ry = info.Rx, info.Ry
+    print(f"[bench] {args.windows} schedule windows: {wall_sched / n_sched * 1e6:.2f} us a step; Rx {Rx} Ry {Ry}",
+          file=sys.stderr, flush=True)
 
-    # ---- per-part timing with HIP events on the launch stream, right after the timed loop.
-    # A pair of events around one launch inside the loop would add the markers' dispatch
-    # latency (about 3.5 us) to a 7.5 us kernel, so each part is timed over a run of
-    # consecutive launches on the same stream and resident batches.
+    # ---- the metric: one instant_backward. Each call has its own resident batch (g_y), the
+    # compressed activation of that batch (under the projections now active) and its own g_x
+    # output, so consecutive calls stream different memory. A timed sample is a run of
+    # CALLS_PER_RUN consecutive calls on the launch stream between two HIP events (a pair of
+    # events around a single call would add the markers' dispatch latency to it); the
+    # per-call time of a sample is the run's time over CALLS_PER_RUN.
     st = torch.cuda.current_stream()
+    xhats = [torch.empty((B, Rx, Cx), dtype=tdt, device=dev) for _ in range(nb)]
+    for t in range(nb):
+        lay.compress_fwd(xs[t], B, xhats[t])
+    gxs = [torch.empty((B, L, Cx), dtype=tdt, device=dev) for _ in range(nb)]
+    torch.cuda.synchronize()
 
+    def run(r):
+        for j in range(CALLS_PER_RUN):
+            t = (r * CALLS_PER_RUN + j) % nb
+            lay.backward(xhats[t], gys[t], w, B, gw, gxs[t])
+
+    for r in range(WARM_RUNS):
+        run(r)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(TIMED_RUNS)]
+    for r in range(TIMED_RUNS):
+        evs[r][0].record(st)
+        run(r)
+        evs[r][1].record(st)
+    torch.cuda.synchronize()
+    per_call = [a.elapsed_time(b) * 1e-3 / CALLS_PER_RUN for a, b in evs]  # seconds
+    t_bwd = quantile(per_call, 0.5)
+    t_bwd_p10, t_bwd_p90 = quantile(per_call, 0.1), quantile(per_call, 0.9)
+    t_bwd_mean = sum(per_call) / len(per_call)
+    print(f"[bench] instant_backward: median {t_bwd * 1e6:.2f} us (p10 {t_bwd_p10 * 1e6:.2f}, "
+          f"p90 {t_bwd_p90 * 1e6:.2f})", file=sys.stderr, flush=True)
+
+    # the same calls captured in a HIP graph and replayed (for comparison)
+    cap = torch.cuda.Stream()
+    cap.wait_stream(st)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        run(0)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        g.replay()
+    gevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+    for a, b in gevs:
+        a.record(st)
+        g.replay()
+        b.record(st)
+    torch.cuda.synchronize()
+    t_bwd_graph = quantile([a.elapsed_time(b) * 1e-3 / CALLS_PER_RUN for a, b in gevs], 0.5)
+    del g
+
+    # ---- the other parts with HIP events on the launch stream over runs of consecutive
+    # launches (a pair of events around one launch would add the markers' dispatch latency)
     def ev_time(fn, reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         fn(0)
@@ -233,18 +323,8 @@ def main():
         e1.synchronize()
         return e0.elapsed_time(e1) / reps * 1e-3  # seconds
 
-    reps = 200
-    t_fwd = ev_time(lambda r: lay.compress_fwd(xs[r % nb], B, xhat), reps)
-    t_bwd = ev_time(lambda r: lay.backward(xhat, gys[r % nb], w, B, gw, gx), reps)
+    t_fwd = ev_time(lambda r: lay.compress_fwd(xs[r % nb], B, xhats[r % nb]), 200)
     t_acc = ev_time(lambda r: lay.calibrate(xs[r % nb], gys[r % nb], B, finalize=False), 50)
-    # host cost of enqueueing one plain step (compress + backward), measured from a drained
-    # queue: when it exceeds the GPU time of a step, the loop above is bound by the host
-    torch.cuda.synchronize()
-    h0 = time.perf_counter()
-    for r in range(50):
-        lay.compress_fwd(xs[r % nb], B, xhat)
-        lay.backward(xhat, gys[r % nb], w, B, gw, gx)
-    t_issue = (time.perf_counter() - h0) / 50
     # one full finalize (eigen-decomposition of both statistics, truncation, publish)
     torch.cuda.synchronize()
     tf0 = time.perf_counter()
@@ -255,70 +335,82 @@ def main():
 
     es = 2 if wl.dtype == "bf16" else 4
     bytes_fwd = es * (B * L * Cx + B * Rx * Cx)
+    # read g_y once, read x_hat and w, write g_w and g_x
     bytes_bwd = es * (B * L * Cy + B * Rx * Cx + 2 * Cx * Cy + B * L * Cx)
     flops_bwd = B * (2 * (Rx + Ry) * L * Cy + 2 * (Rx + Ry) * Cx * Cy + 2 * Ry * L * Cx)
     # statistics: the upper triangle of both L x L sums per batch (the mirror earns no credit)
     flops_acc = L * (L + 1) * B * (Cx + Cy)
-    gbs_fwd = bytes_fwd / t_fwd / 1e9
+    gbs_bwd = bytes_bwd / t_bwd / 1e9
+    gbs_bwd_mean = bytes_bwd / t_bwd_mean / 1e9
 
     headline = wl.name == "bert_attn"
-    ms_per_step = wall / args.steps * 1e3
-    tokens = args.steps * B * L
-    value = tokens / wall
-
+    wname = f"{WORKLOAD_NAMES.get(wl.name, wl.name)} linear{'' if len(wl.layers) == 1 else ' (' + ly.name + ')'}"
     out = {
         "metric": ("low-rank backward tokens/s + achieved HBM GB/s (% peak), BERT-base linear" if headline else
                    f"low-rank backward tokens/s + achieved HBM GB/s (% peak), {wl.name} linear"),
-        "value": value,
+        "value": B * L / t_bwd,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": wall / args.steps * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{WORKLOAD_NAMES.get(wl.name, wl.name)} linear{'' if len(wl.layers) == 1 else ' (' + ly.name + ')'}, "
-                               f"B={B} L={L} Cx={Cx} Cy={Cy}, "
+        "config": {"workload": f"{wname}, B={B} L={L} Cx={Cx} Cy={Cy}, "
                                f"eps={wl.eps} p={wl.p} N_cal={wl.n_cal} N_t={wl.n_t}",
                    "global_batch": B, "seq_len": L, "parallelism": "single GPU",
-                   "step": "compress + low-rank backward every step; statistics on the first N_cal steps of "
-                           "each N_t window; eigen-decomposition + truncation once per window",
+                   "value": "B*L / median time of one instant_backward (a5-a8): HIP events around runs of "
+                            f"{CALLS_PER_RUN} consecutive calls on rotating resident batches, {TIMED_RUNS} timed "
+                            "runs after 20 untimed ones",
+                   "step": "ms_per_step: compress + low-rank backward every step; statistics on the first N_cal "
+                           "steps of each N_t window; eigen-decomposition + truncation once per window",
                    "streams": "statistics and finalize on a side stream" if not args.one_stream else "one stream",
                    "finalize": "synchronous" if args.sync_finalize else
                                "asynchronous (new projections from the first forward after it completes)",
                    "Rx": Rx, "Ry": Ry, "kx": info.kx, "ky": info.ky},
         "parts": {
-            "compress_fwd_us": t_fwd * 1e6, "compress_fwd_GBs": gbs_fwd,
-            "backward_us": t_bwd * 1e6, "backward_GBs": bytes_bwd / t_bwd / 1e9,
-            "backward_pct_hbm_peak": 100.0 * bytes_bwd / t_bwd / 1e9 / HBM_PEAK_GBS,
-            "backward_tokens_per_s": B * L / t_bwd, "backward_TFLOPs": flops_bwd / t_bwd / 1e12,
+            "backward_us_median": t_bwd * 1e6, "backward_us_p10": t_bwd_p10 * 1e6,
+            "backward_us_p90": t_bwd_p90 * 1e6, "backward_us_mean": t_bwd_mean * 1e6,
+            "backward_GBs": gbs_bwd, "backward_pct_hbm_peak": 100.0 * gbs_bwd / HBM_PEAK_GBS,
+            "backward_tokens_per_s_p10_p90": [B * L / t_bwd_p90, B * L / t_bwd_p10],
+            "backward_TFLOPs": flops_bwd / t_bwd / 1e12,
+            "backward_algorithmic_bytes": bytes_bwd,
+            "backward_us_graph_replay_median": t_bwd_graph * 1e6,
+            "compress_fwd_us": t_fwd * 1e6, "compress_fwd_GBs": bytes_fwd / t_fwd / 1e9,
+            "compress_fwd_pct_hbm_peak": 100.0 * bytes_fwd / t_fwd / 1e9 / HBM_PEAK_GBS,
             "statistics_per_batch_us": t_acc * 1e6,
             "statistics_TFLOPs": flops_acc / t_acc / 1e12,
             "statistics_pct_mfma_bf16_peak" if wl.dtype == "bf16" else "statistics_pct_mfma_fp32_peak":
                 100.0 * flops_acc / t_acc / 1e12 / (MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else
                                                     MFMA_FP32_PEAK_TFLOPS),
             "statistics_GBs": es * B * L * (Cx + Cy) / t_acc / 1e9,
+            "schedule_tokens_per_s": n_sched * B * L / wall_sched,
+            "schedule_us_per_step": wall_sched / n_sched * 1e6,
+            "schedule_windows": args.windows,
             "eigensolver": solver_used,
             "cold_finalize_ms": t_cold * 1e3,
             "finalize_ms": t_fin * 1e3,
-            "finalize_in_loop_ms": (sum(fin_loop) / len(fin_loop) * 1e3) if fin_loop else None,
-            "finalizes_in_loop": len(fin_loop), "host_enqueue_us_per_plain_step": t_issue * 1e6, "jacobi_sweeps": [info2.sweeps_x, info2.sweeps_g],
-            "finalize_status": rcb.instant_status_str(s),
+            "finalize_in_window_ms": (sum(fin_loop) / len(fin_loop) * 1e3) if fin_loop else None,
             "finalizes_published": f"{published}/{len(fin_events)}",
+            "jacobi_sweeps": [info2.sweeps_x, info2.sweeps_g],
+            "finalize_status": rcb.instant_status_str(s),
         },
-        "roofline": {"kernel": "proj (forward compression x_hat = P x)", "bound": "hbm",
-                     "achieved": gbs_fwd, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs_fwd / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "launch_us": t_fwd * 1e6, "launches_timed": reps,
-                     "algorithmic_bytes_per_launch": bytes_fwd},
+        "roofline": {"kernel": "instant_backward: stacked projection [P;Q] g_y + the g_w / g_hat_x / expansion "
+                               "kernels, one call", "bound": "hbm",
+                     "achieved": gbs_bwd_mean, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs_bwd_mean / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name + "/" + ly.name),
+                     "launch_us_mean": t_bwd_mean * 1e6, "calls_timed": TIMED_RUNS * CALLS_PER_RUN,
+                     "algorithmic_bytes_per_call": bytes_bwd},
     }
 
     if not args.no_cpu_baseline and headline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
     print(json.dumps(out), flush=True)
+    torch.cuda.synchronize()
+    lay.close()
 
 
 # The linear layers of one BERT-base encoder layer (B=32, L=512, bf16): the four attention
@@ -420,11 +512,16 @@ def bench_block(args):
                      "activation_memory_ratio": tot["act_bytes_exact"] / tot["act_bytes_instant"]},
            "layers": out_layers}
     print(json.dumps(res), flush=True)
+    torch.cuda.synchronize()
+    for c in layers:
+        c["lay"].close()
 
 
 def cpu_baseline(wl, nsample):
-    """The CPU oracle (float64 numpy) timed on a bounded sample of the same step."""
-    import numpy as np
+    """The CPU oracle (float64 numpy), as it stands, timed on a bounded sample of the same
+    workload: its low-rank backward (a5-a8, the metric's work) on `nsample` samples of one
+    batch, scaled to tokens/s; and, for context, its whole per-step schedule."""
+    import numpy as np  # noqa: F401
 
     import oracle as O
     import workloads as W
@@ -433,15 +530,17 @@ def cpu_baseline(wl, nsample):
         cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
-    ly = wl.layer(0)
     d = W.make_layer_batch(wl, 0, 0, with_w=True)
     xs, gys, w = d["x64"][:nsample], d["gy64"][:nsample], d["w64"]
     cal = O.calibrate([d["x64"]], [d["gy64"]], wl.eps, wl.p, O.COMP_PAPER)
     P, Q = cal["x"]["P"], cal["g"]["P"]
-    t0 = time.perf_counter()
     xh = O.compress(P, xs)
+    t0 = time.perf_counter()
     O.backward(P, Q, xh, gys, w)
-    t_cb = (time.perf_counter() - t0) / nsample            # per sample
+    t_bwd = (time.perf_counter() - t0) / nsample           # per sample
+    t0 = time.perf_counter()
+    O.compress(P, xs)
+    t_cmp = (time.perf_counter() - t0) / nsample           # per sample
     t0 = time.perf_counter()
     acc = O.Accumulator(wl.L)
     acc.add(xs)
@@ -451,12 +550,13 @@ def cpu_baseline(wl, nsample):
     O.calibrate_side(cal["C_X"], wl.eps, wl.p, O.COMP_PAPER, wl.L)
     O.calibrate_side(cal["C_G"], wl.eps, wl.p, O.COMP_PAPER, wl.L)
     t_fin = time.perf_counter() - t0                        # per finalize
-    per_step = wl.B * t_cb + (wl.n_cal / wl.n_t) * wl.B * t_acc + t_fin / wl.n_t
-    return {"value": wl.B * wl.L / per_step, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{nsample} of {wl.B} samples of one batch for compress+backward and the statistics, "
-                      f"one full finalize (eigh of both {wl.L}x{wl.L} statistics); per-step time = "
-                      f"B*t_sample(compress+backward) + (N_cal/N_t)*B*t_sample(statistics) + t_finalize/N_t",
-            "seconds_per_step": per_step}
+    per_step = wl.B * (t_cmp + t_bwd) + (wl.n_cal / wl.n_t) * wl.B * t_acc + t_fin / wl.n_t
+    return {"value": wl.L / t_bwd, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"the oracle's low-rank backward (P g_y, Q g_y, g_w, g_hat_x, expansion) on {nsample} of "
+                      f"{wl.B} samples of one batch: tokens/s = {nsample}*L / time",
+            "schedule_tokens_per_s": wl.B * wl.L / per_step,
+            "schedule_sample": f"per step B*t_sample(compress + backward) + (N_cal/N_t)*B*t_sample(statistics) "
+                               f"+ t_finalize/N_t, with one full finalize (eigh of both {wl.L}x{wl.L} statistics)"}
 
 
 if __name__ == "__main__":

@@ -26,12 +26,16 @@
  *     allocates device memory: all device state lives in the caller's workspace
  *     (instant_workspace_bytes). The host handle is the library's own.
  *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL is the
- *     default stream), except a finalizing instant_calibrate, which returns only when
- *     the new projections (or the failure) are known: the ranks Rx, Ry it decides size
- *     every later launch. A finalize happens once per N_t steps ([Framework]).
+ *     default stream). The exception is a synchronous finalize (instant_calibrate with
+ *     INSTANT_FINALIZE_SYNC), which returns only when the new projections (or the
+ *     failure) are known: the ranks Rx, Ry it decides size every later launch. An
+ *     asynchronous finalize (INSTANT_FINALIZE_ASYNC) returns at once; its outcome is
+ *     applied later (see instant_calibrate). A finalize happens once per N_t steps
+ *     ([Framework]).
  *   - Host-detectable errors return at once with no side effect.
- *     Device-detected calibration failures are latched; the previous projections
- *     stay active and instant_query reports the failure.
+ *     Calibration failures found on the device (and a finalize whose launch failed or
+ *     whose bounded eigensolver wait gave up, E_HIP) are latched: the previous
+ *     projections stay active and instant_query reports the failure.
  *   - The I/O dtype (x, gy, w, xhat, gw, gx) is fixed per handle: float32 or
  *     bfloat16. Accumulation is float32; statistics are summed in float64 across
  *     batches.

@@ -12,8 +12,11 @@ Importing fails loudly when the built library is missing; there is no fallback.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
+import sys
+import weakref
 
 try:  # bind to the HIP runtime PyTorch has already loaded, if PyTorch is present
     import torch  # noqa: F401
@@ -172,33 +175,63 @@ def make_config(L, Cx, Cy, B_max, R_max=64, p=2, N_t=100, eps=0.95, dtype="bf16"
                           float(eps), dt, cp, int(max_sweeps), sv, int(sub_iters))
 
 
+# Handles still open. They are closed at interpreter exit by an atexit hook, which runs
+# before the interpreter tears down its modules and long before the HIP runtime's own
+# teardown at process exit: instant_destroy (an event wait, hipEventDestroy, hipHostFree)
+# must not run once that teardown has begun.
+_LIVE = weakref.WeakSet()
+
+
+def close_all() -> None:
+    """Close every InstantLayer still open (their workspaces stay with their owners)."""
+    for lay in list(_LIVE):
+        lay.close()
+
+
+atexit.register(close_all)
+
+
 class InstantLayer:
-    """Owns one handle and its device workspace (a uint8 tensor on the current device)."""
+    """Owns one handle and its device workspace (a uint8 tensor on the current device).
+
+    Close it with close() (or use it as a context manager); handles still open at
+    interpreter exit are closed by an atexit hook, and a garbage-collected handle is closed
+    by __del__ unless the interpreter is already finalizing."""
 
     def __init__(self, cfg: instant_config, device="cuda", stream=None):
         self.cfg = cfg
+        self.h = None
         n = instant_workspace_bytes(cfg)
         if n == 0:
             raise InstantError(INSTANT_E_ARG, "instant_workspace_bytes")
         self.workspace = torch.empty(n + 256, dtype=torch.uint8, device=device)
         base = self.workspace.data_ptr()
         self._ws_ptr = (base + 255) // 256 * 256
-        s, self.h = instant_create(cfg, self._ws_ptr, stream)
+        s, h = instant_create(cfg, self._ws_ptr, stream)
         if s != INSTANT_OK:
             raise InstantError(s, "instant_create")
+        self.h = h
+        _LIVE.add(self)
 
     def close(self):
         if getattr(self, "h", None):
             instant_destroy(self.h)
             self.h = None
+        _LIVE.discard(self)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+        return False
 
     def __del__(self):
-        # at interpreter shutdown the module's globals may already be gone; the process
-        # exit releases the handle then
-        try:
-            self.close()
-        except TypeError:
-            pass
+        # during interpreter finalization the HIP runtime may be going away: leave the
+        # small host handle to the process exit (the atexit hook has closed it already)
+        if sys.is_finalizing():
+            return
+        self.close()
 
     def _check(self, s, where):
         if s != INSTANT_OK:

@@ -357,8 +357,12 @@ INSTANT_API instant_status instant_calibrate(instant_layer* h, const void* x, co
                                  h->cfg.max_sweeps, h->warm, h->ws + h->lay.eig, out, h->hflags, st, !async);
   if (e == hipSuccess && async) e = hipEventRecord(h->done, st);
   if (e != hipSuccess) {
+    // a failed launch, or a bounded eigensolver wait that gave up: latched like any other
+    // calibration failure, so instant_query reports it; the previous projections stay active
     h->warm = false;
     h->nx = h->ng = 0;
+    h->last = INSTANT_E_HIP;
+    h->info.status = INSTANT_E_HIP;
     return INSTANT_E_HIP;
   }
   h->pend_t = t;

@@ -839,13 +839,14 @@ __global__ __launch_bounds__(1024) void truncate_build_kernel(TruncArgs a, int l
     double Sk = 0.0, SR = 0.0;
     if (status == 0 && !(E > 0.0)) status = (E == 0.0) ? 5 : 6;
     if (status == 0) {
+      // With all L values known, E = pre[n - 1] and eps <= 1 put the threshold at or below
+      // pre[n - 1] (a product by a float no greater than 1 rounds to at most E), so some
+      // index always qualifies. Only a subspace basis can miss it: eps * E then lies beyond
+      // the n directions it holds.
       if (kfirst < n) {
         k = kfirst + 1;
         Sk = pre[kfirst];
-      } else if (!a.E_ext) {  // rounding made the total fall short of eps*E: only possible at eps == 1
-        k = L;
-        Sk = E;
-      } else {  // the energy threshold lies beyond the n directions the subspace holds
+      } else {
         status = 4;
       }
     }

@@ -68,10 +68,18 @@ class InstantLinear(torch.nn.Module):
 
     dtype is the library's I/O dtype ("bf16" or "fp32"); inputs and the weight must have
     it. N_cal calibration steps start every window of N_t steps (N_cal <= N_t).
+
+    comp is the energy compensation of the projections (关键设计 2). The default is the
+    ratio reading, c = (E / sum_{i<=R} sigma_i^2)^(1/2) >= 1, which keeps the compressed
+    steps' gradients on the scale of the exact ones. The factor as printed ("paper",
+    c = (sum_{i<=R} sigma_i^2)^(-1/2)) carries the units of the data: g_w scales by c_P^2
+    and g_x by c_Q^2 (about 5e-11 on BERT-sized synthetic data), so the compressed steps of a
+    window would get gradients on a different scale from its exact calibration steps; it
+    stays selectable. "none" (c = 1) gives the orthogonal projection.
     """
 
     def __init__(self, L, Cx, Cy, B_max, N_t=100, N_cal=16, p=2, eps=0.95, dtype="bf16", R_max=64,
-                 comp="paper", weight=None, device="cuda"):
+                 comp="ratio", weight=None, device="cuda"):
         super().__init__()
         if not 1 <= N_cal <= N_t:
             raise ValueError("need 1 <= N_cal <= N_t")

@@ -21,7 +21,7 @@ torch = pytest.importorskip("torch")
 @pytest.mark.timeout(600)
 def test_llm_mlp_calibration_and_backward():
     import rank_compressed_backprop_amd as rcb
-    from gpu_util import TOL, empty, from_dev, rel, to_dev
+    from gpu_util import check_close, empty, from_dev, oracle_magnitudes, rel, to_dev
     wl = W.get_workload("llm_mlp")
     ly = wl.layer(0)
     L, B = wl.L, wl.B
@@ -32,6 +32,12 @@ def test_llm_mlp_calibration_and_backward():
     # the subspace eigensolver on the same batches (top m = 80 eigenpairs, 关键设计 2)
     lay_s = rcb.InstantLayer(rcb.make_config(L, ly.Cx, ly.Cy, B, R_max=64, p=wl.p, eps=wl.eps, dtype=wl.dtype,
                                              comp="paper", solver="subspace"))
+    # the other two readings of the compensation (关键设计 2), one with each eigensolver
+    lay_r = rcb.InstantLayer(rcb.make_config(L, ly.Cx, ly.Cy, B, R_max=64, p=wl.p, eps=wl.eps, dtype=wl.dtype,
+                                             comp="ratio"))
+    lay_n = rcb.InstantLayer(rcb.make_config(L, ly.Cx, ly.Cy, B, R_max=64, p=wl.p, eps=wl.eps, dtype=wl.dtype,
+                                             comp="none", solver="subspace"))
+    extra = (("ratio", lay_r), ("none", lay_n))
     rng = np.random.default_rng(5)
     m = 256
     rows = np.concatenate([rng.integers(0, L, m), np.arange(0, L, L // 16)])
@@ -43,8 +49,8 @@ def test_llm_mlp_calibration_and_backward():
         ex_x += O.autocorr_entries([d["x64"]], rows, cols) * B
         ex_g += O.autocorr_entries([d["gy64"]], rows, cols) * B
         xd, gd = to_dev(d["x"], wl.dtype), to_dev(d["gy"], wl.dtype)
-        assert lay.calibrate(xd, gd, B, finalize=False) == 0
-        assert lay_s.calibrate(xd, gd, B, finalize=False) == 0
+        for ll in (lay, lay_s, lay_r, lay_n):
+            assert ll.calibrate(xd, gd, B, finalize=False) == 0
         del d, xd, gd
     n = wl.n_cal * B
     CX = torch.empty((L, L), dtype=torch.float64, device="cuda")
@@ -67,6 +73,9 @@ def test_llm_mlp_calibration_and_backward():
     t2 = time.perf_counter()
     print(f"  cold finalize: jacobi {1e3 * (t1 - t0):.1f} ms, subspace {1e3 * (t2 - t1):.1f} ms", flush=True)
     assert s2 == rcb.INSTANT_OK, rcb.instant_status_str(s2)
+    for tag, ll in extra:
+        s3 = ll.calibrate(None, None, 0, finalize=True)
+        assert s3 == rcb.INSTANT_OK, (tag, rcb.instant_status_str(s3))
     _, info = lay.query()
     ox = O.calibrate_side(CX, wl.eps, wl.p, O.COMP_PAPER, 64)
     og = O.calibrate_side(CG, wl.eps, wl.p, O.COMP_PAPER, 64)
@@ -104,8 +113,31 @@ def test_llm_mlp_calibration_and_backward():
     torch.cuda.synchronize()
     xh_o = O.compress(ox["P"], d["x64"])
     out = O.backward(ox["P"], og["P"], xh_o, d["gy64"], d["w64"])
-    tol = TOL[wl.dtype]
-    e = (rel(from_dev(xhat, wl.dtype), xh_o), rel(from_dev(gw, wl.dtype), out["gw"]),
-         rel(from_dev(gx, wl.dtype), out["gx"]))
-    print("  end-to-end rel err xhat %.2e gw %.2e gx %.2e (tol %g)" % (*e, tol), flush=True)
-    assert max(e) <= tol
+    xh_m, out_m = oracle_magnitudes(O, ox["P"], og["P"], d["x64"], d["gy64"], d["w64"])
+    dt = wl.dtype
+    msg = [check_close("xhat", from_dev(xhat, dt), xh_o, dt, xh_m),
+           check_close("gw", from_dev(gw, dt), out["gw"], dt, out_m["gw"]),
+           check_close("gx", from_dev(gx, dt), out["gx"], dt, out_m["gx"])]
+    print("  end-to-end rel err Frobenius/per-element: " + ", ".join(msg), flush=True)
+
+    # the other compensations: the same decomposition and ranks, P = c U_R^T with the mode's c.
+    # The oracle's products are bilinear in P and in Q, so its outputs for a mode are the
+    # printed-compensation outputs times (c_mode / c_paper) (x_hat), (c_mode / c_paper)^2
+    # (g_w through P twice, g_x through Q twice).
+    comp_id = {"ratio": O.COMP_RATIO, "none": O.COMP_NONE}
+    for tag, ll in extra:
+        _, inf = ll.query()
+        assert (inf.kx, inf.Rx, inf.ky, inf.Ry) == (ox["k"], ox["R"], og["k"], og["R"]), tag
+        cs = []
+        for o, c_gpu in ((ox, inf.cP), (og, inf.cQ)):
+            st, _, _, prefix = O.truncate(o["sigma"], O.eps_as_f32(wl.eps), wl.p)
+            c = O.compensation(prefix, o["R"], comp_id[tag])
+            assert abs(c_gpu - c) <= 1e-5 * c, (tag, c_gpu, c)
+            cs.append(c / o["c"])
+        ll.compress_fwd(x, B, xhat)
+        ll.backward(xhat, gy, w, B, gw, gx)
+        torch.cuda.synchronize()
+        msg = [check_close("xhat", from_dev(xhat, dt), cs[0] * xh_o, dt, cs[0] * xh_m),
+               check_close("gw", from_dev(gw, dt), cs[0] ** 2 * out["gw"], dt, cs[0] ** 2 * out_m["gw"]),
+               check_close("gx", from_dev(gx, dt), cs[1] ** 2 * out["gx"], dt, cs[1] ** 2 * out_m["gx"])]
+        print(f"  comp {tag}: c_P {inf.cP:.4g} c_Q {inf.cQ:.4g}; " + ", ".join(msg), flush=True)

@@ -68,8 +68,9 @@ def test_schedule_and_gradients_fp32():
         if mode == "finalize":
             # the window's projections come from its own calibration steps only
             w0 = s - (N_cal - 1)
+            # (the layer's default compensation is the ratio reading)
             cal = O.calibrate([batches[t]["x64"] for t in range(w0, s + 1)],
-                              [batches[t]["gy64"] for t in range(w0, s + 1)], wl.eps, wl.p, O.COMP_PAPER, R_max)
+                              [batches[t]["gy64"] for t in range(w0, s + 1)], wl.eps, wl.p, O.COMP_RATIO, R_max)
             assert mod.last_status == 0, mod.status()
             assert (mod.Rx, mod.Ry) == (cal["x"]["R"], cal["g"]["R"])
             P = torch.empty((mod.Rx, L), dtype=torch.float32, device="cuda")
@@ -114,7 +115,7 @@ def test_gradient_error_against_exact_as_p_varies():
     subspace between two windows at p = 2.
 
     The error is measured with the compensation off (P = U_R^T, an orthogonal projector)
-    and with the ratio reading: the printed compensation (the library's default) scales
+    and with the ratio reading (the layer's default): the printed compensation scales
     g_w by c_P^2 and g_x by c_Q^2 with c = S_R^(-1/2), a scalar with units that makes the
     raw error against the exact gradient meaningless. With the compensation off, more
     oversampling keeps more of the spectrum, so the error may not grow with p."""
@@ -164,6 +165,23 @@ def test_gradient_error_against_exact_as_p_varies():
         ea, eb = errs[("none", a)], errs[("none", b)]
         assert eb[2] >= ea[2]
         assert eb[0] <= ea[0] * 1.02 and eb[1] <= ea[1] * 1.02
+    # the layer's default compensation keeps a compressed step's gradients on the scale of the
+    # exact gradients of the same step (the printed factor would shrink them by c^2 ~ 1e-11)
+    import rank_compressed_backprop_amd as rcb
+    mod = InstantLinear(L, ly.Cx, ly.Cy, B, N_t=N_t, N_cal=N_cal, p=2, eps=wl.eps, dtype="bf16", weight=w)
+    assert mod.layer.cfg.comp == rcb.INSTANT_COMP_RATIO
+    for s in range(N_t):
+        x, gy = data[s]
+        gx, gw = _step(mod, x, gy)
+        if mod.mode_of_step(s) == "compress":
+            xf, gf = x.float().reshape(-1, ly.Cx), gy.float().reshape(-1, ly.Cy)
+            r_w = float(torch.linalg.norm(gw.float()) / torch.linalg.norm(gf.t().contiguous() @ xf))
+            r_x = float(torch.linalg.norm(gx.float()) / torch.linalg.norm(gf @ w32))
+            print(f"  default compensation, step {s}: |g_w| / |g_w exact| {r_w:.3f}, "
+                  f"|g_x| / |g_x exact| {r_x:.3f}", flush=True)
+            assert 0.5 <= r_w <= 2.0 and 0.5 <= r_x <= 2.0
+    mod.layer.close()
+
     P1, P2 = proj
     k = min(P1.shape[0], P2.shape[0])
     U1 = np.linalg.qr(P1[:k].T)[0]
