@@ -170,6 +170,25 @@ instant_status instant_compress_fwd(instant_layer* h, const void* x, int32_t B, 
 instant_status instant_backward(instant_layer* h, const void* xhat, const void* gy, const void* w,
                                 int32_t B, void* gw, void* gx, void* stream);
 
+/* For callers that cannot allocate device memory at the time of the call (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): instant_backward
+ * with its per-call intermediates (P gy, Q gy, g_hat_x and the float32 K-slice partials of
+ * g_hat_x, which instant_backward keeps in the handle's workspace) in a static device array
+ * of INSTANT_STATIC_SCRATCH_BYTES that the library holds on every device it runs on until
+ * the process ends. Same arguments, same kernels and the same results, bit for bit, as
+ * instant_backward; no allocation of any kind.
+ * The call needs align256(B*Rx*Cy*s) + align256(B*Ry*Cy*s) + align256(B*Ry*Cx*s) bytes,
+ * plus the float32 partials when w is too large for L2 (s = bytes per I/O element,
+ * align256 = rounded up to 256), and returns E_SHAPE when that exceeds
+ * INSTANT_STATIC_SCRATCH_BYTES (64 MiB covers B=8, L=2048, Cx=4096, Cy=11008 at Rx=Ry=34).
+ * Nothing in the scratch needs to start at zero: every byte read is written earlier in the
+ * same call. All calls on one GPU share its array, so calls that overlap on one GPU (other
+ * streams, other handles, other threads) race; order them. Errors: E_ARG, E_SHAPE, E_STATE,
+ * E_HIP (also when the array's device address could not be looked up at instant_create). */
+#define INSTANT_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+instant_status instant_backward_static(instant_layer* h, const void* xhat, const void* gy, const void* w,
+                                       int32_t B, void* gw, void* gx, void* stream);
+
 /* Report the result of the last finalize (ranks, compensation, sweeps, status).
  * Returns that finalize's status (INSTANT_OK if none has failed). Host only. */
 instant_status instant_query(instant_layer* h, instant_info* out);

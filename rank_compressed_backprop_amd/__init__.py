@@ -72,6 +72,7 @@ _sig = {
     "instant_calibrate": (_st, [_vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp]),
     "instant_compress_fwd": (_st, [_vp, _vp, ctypes.c_int32, _vp, _vp]),
     "instant_backward": (_st, [_vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp]),
+    "instant_backward_static": (_st, [_vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp]),
     "instant_query": (_st, [_vp, ctypes.POINTER(instant_info)]),
     "instant_set_projections": (_st, [_vp, _vp, ctypes.c_int32, _vp, ctypes.c_int32, _vp]),
     "instant_get_projections": (_st, [_vp, _vp, _vp, _vp, _vp, _vp]),
@@ -141,6 +142,14 @@ def instant_compress_fwd(h, x, B: int, xhat, stream=None) -> int:
 
 def instant_backward(h, xhat, gy, w, B: int, gw, gx, stream=None) -> int:
     return _lib.instant_backward(h, _ptr(xhat), _ptr(gy), _ptr(w), int(B), _ptr(gw), _ptr(gx), _stream(stream))
+
+
+def instant_backward_static(h, xhat, gy, w, B: int, gw, gx, stream=None) -> int:
+    return _lib.instant_backward_static(h, _ptr(xhat), _ptr(gy), _ptr(w), int(B), _ptr(gw), _ptr(gx),
+                                        _stream(stream))
+
+
+INSTANT_STATIC_SCRATCH_BYTES = 64 << 20  # include/instant.h
 
 
 def instant_query(h):
@@ -248,6 +257,9 @@ class InstantLayer:
 
     def backward(self, xhat, gy, w, B, gw, gx, stream=None):
         self._check(instant_backward(self.h, xhat, gy, w, B, gw, gx, stream), "instant_backward")
+
+    def backward_static(self, xhat, gy, w, B, gw, gx, stream=None):
+        self._check(instant_backward_static(self.h, xhat, gy, w, B, gw, gx, stream), "instant_backward_static")
 
     def query(self):
         return instant_query(self.h)

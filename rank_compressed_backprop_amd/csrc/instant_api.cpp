@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "instant.h"
@@ -123,6 +124,35 @@ Layout layout_of(const instant_config* c) {
   return l;
 }
 
+// ---- the scratch of instant_backward_static: one file-scope device array per GPU, held by
+// every device the library runs on until the process ends. Host code never uses the
+// array's name as an address: its device address is looked up once per device (at the first
+// instant_create on that device) and kept in scratch_ptr.
+constexpr size_t STATIC_SCRATCH_BYTES = INSTANT_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[STATIC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES];
+bool scratch_looked_up[MAX_DEVICES];
+
+// The device address of `scratch` on device `dev` (the current device), looked up on the
+// first call for that device; nullptr if the lookup failed.
+void* scratch_on(int dev) {
+  if (dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_looked_up[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();  // leave no sticky error behind for the caller's next call
+      p = nullptr;
+    }
+    scratch_ptr[dev] = p;
+    scratch_looked_up[dev] = true;
+  }
+  return scratch_ptr[dev];
+}
+
 }  // namespace
 
 struct instant_layer {
@@ -135,6 +165,7 @@ struct instant_layer {
   int Rx, Ry;
   int64_t nx, ng;
   int ncu;  // compute units of the device the handle was created on
+  void* scratch;  // device address of the static scratch on that device (null if unavailable)
   instant_info info;
   instant_status last;
   // outcome of the last finalize: copied by the device into pinned host memory; with an
@@ -269,6 +300,7 @@ INSTANT_API instant_status instant_create(instant_layer** h, const instant_confi
   }
   int dev = 0;
   L->ncu = 0;
+  L->scratch = nullptr;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&L->ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || L->ncu < 1) {
     (void)hipEventDestroy(L->done);
@@ -276,6 +308,7 @@ INSTANT_API instant_status instant_create(instant_layer** h, const instant_confi
     delete L;
     return INSTANT_E_HIP;
   }
+  L->scratch = scratch_on(dev);
   // statistics start at zero; the rest of the workspace is written before it is read
   hipError_t e = launch_zero(L->SX(), (size_t)cfg->L * cfg->L * sizeof(double), S(stream));
   if (e == hipSuccess) e = launch_zero(L->ws + L->lay.zpad, 256, S(stream));
@@ -390,34 +423,83 @@ INSTANT_API instant_status instant_compress_fwd(instant_layer* h, const void* x,
                             S(stream)));
 }
 
+namespace {
+
+// Where one backward call keeps its intermediates: P g_y [B][Rx][Cy], Q g_y [B][Ry][Cy],
+// g_hat_x [B][Ry][Cx] (I/O dtype) and the float32 K-slice partials of g_hat_x.
+struct BwdScratch {
+  void* Pgy;
+  void* Qgy;
+  void* gxh;
+  float* gpart;
+  size_t gpart_floats;
+};
+
+// The low-rank backward of one call (the launches of instant_backward).
+instant_status run_backward(instant_layer* h, const void* xhat, const void* gy, const void* w, int B, void* gw,
+                            void* gx, const BwdScratch& sc, hipStream_t st) {
+  const int a = h->active;
+  const int L = h->cfg.L, Cx = h->cfg.Cx, Cy = h->cfg.Cy, Rx = h->Rx, Ry = h->Ry;
+  // [P; Q] gy_b from one pass over gy
+  hipError_t e = launch_proj(h->bf16, h->PQ(a), h->lay.ldL, Rx + Ry, Rx, gy, B, L, Cy, sc.Pgy, sc.Qgy, st);
+  if (gx_fused_applies(h->bf16, B, Cx, Cy)) {
+    // g_x_b = Q^T ((Q gy_b) w) with w resident in L2, and g_w, in one launch
+    if (e == hipSuccess)
+      e = launch_bwd_tail(h->bf16, sc.Qgy, w, h->Qt(a), LD_QT, B, Ry, L, Cy, Cx, gx, sc.Pgy, xhat, gw, B * Rx,
+                          h->ncu, st);
+  } else {
+    // g_w = sum_b (P gy_b)^T x_hat_b: M = Cy, N = Cx, K = B * Rx
+    if (e == hipSuccess)
+      e = launch_gemm(h->bf16, true, sc.Pgy, Cy, 0, xhat, Cx, 0, gw, Cx, 0, 1, Cy, Cx, B * Rx, st);
+    // g_hat_x = (Q gy) w: M = B * Ry, N = Cx, K = Cy
+    if (e == hipSuccess)
+      e = launch_gemm(h->bf16, false, sc.Qgy, Cy, 0, w, Cx, 0, sc.gxh, Cx, 0, 1, B * Ry, Cx, Cy, st, sc.gpart,
+                      sc.gpart_floats, h->ws + h->lay.zpad);
+    // g_x_b = Q^T g_hat_x_b
+    if (e == hipSuccess) e = launch_expand(h->bf16, h->Qt(a), LD_QT, sc.gxh, B, Ry, L, Cx, gx, st);
+  }
+  return hip_ok(e);
+}
+
+}  // namespace
+
 INSTANT_API instant_status instant_backward(instant_layer* h, const void* xhat, const void* gy, const void* w,
                                             int32_t B, void* gw, void* gx, void* stream) {
   if (!h || !xhat || !gy || !w || !gw || !gx || B < 1) return INSTANT_E_ARG;
   if (B > h->cfg.B_max) return INSTANT_E_SHAPE;
   if (h->active < 0) return INSTANT_E_STATE;
-  const int a = h->active;
-  const int L = h->cfg.L, Cx = h->cfg.Cx, Cy = h->cfg.Cy, Rx = h->Rx, Ry = h->Ry;
-  hipStream_t st = S(stream);
-  void* Pgy = h->ws + h->lay.Pgy;
-  void* Qgy = h->ws + h->lay.Qgy;
-  void* gxh = h->ws + h->lay.gxh;
-  // [P; Q] gy_b from one pass over gy
-  hipError_t e = launch_proj(h->bf16, h->PQ(a), h->lay.ldL, Rx + Ry, Rx, gy, B, L, Cy, Pgy, Qgy, st);
-  if (gx_fused_applies(h->bf16, B, Cx, Cy)) {
-    // g_x_b = Q^T ((Q gy_b) w) with w resident in L2, and g_w, in one launch
-    if (e == hipSuccess)
-      e = launch_bwd_tail(h->bf16, Qgy, w, h->Qt(a), LD_QT, B, Ry, L, Cy, Cx, gx, Pgy, xhat, gw, B * Rx, h->ncu, st);
-  } else {
-    // g_w = sum_b (P gy_b)^T x_hat_b: M = Cy, N = Cx, K = B * Rx
-    if (e == hipSuccess) e = launch_gemm(h->bf16, true, Pgy, Cy, 0, xhat, Cx, 0, gw, Cx, 0, 1, Cy, Cx, B * Rx, st);
-    // g_hat_x = (Q gy) w: M = B * Ry, N = Cx, K = Cy
-    if (e == hipSuccess)
-      e = launch_gemm(h->bf16, false, Qgy, Cy, 0, w, Cx, 0, gxh, Cx, 0, 1, B * Ry, Cx, Cy, st,
-                      (float*)(h->ws + h->lay.gpart), h->lay.gpart_floats, h->ws + h->lay.zpad);
-    // g_x_b = Q^T g_hat_x_b
-    if (e == hipSuccess) e = launch_expand(h->bf16, h->Qt(a), LD_QT, gxh, B, Ry, L, Cx, gx, st);
-  }
-  return hip_ok(e);
+  const BwdScratch sc{h->ws + h->lay.Pgy, h->ws + h->lay.Qgy, h->ws + h->lay.gxh, (float*)(h->ws + h->lay.gpart),
+                      h->lay.gpart_floats};
+  return run_backward(h, xhat, gy, w, B, gw, gx, sc, S(stream));
+}
+
+INSTANT_API instant_status instant_backward_static(instant_layer* h, const void* xhat, const void* gy,
+                                                   const void* w, int32_t B, void* gw, void* gx, void* stream) {
+  if (!h || !xhat || !gy || !w || !gw || !gx || B < 1) return INSTANT_E_ARG;
+  if (B > h->cfg.B_max) return INSTANT_E_SHAPE;
+  if (h->active < 0) return INSTANT_E_STATE;
+  if (!h->scratch) return INSTANT_E_HIP;  // the device address of the scratch could not be looked up
+  const size_t esz = h->bf16 ? 2 : 4;
+  const size_t Cx = h->cfg.Cx, Cy = h->cfg.Cy, Rx = h->Rx, Ry = h->Ry;
+  // the same intermediates instant_backward keeps in the workspace, packed for this call
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  const size_t o_pgy = take((size_t)B * Rx * Cy * esz);
+  const size_t o_qgy = take((size_t)B * Ry * Cy * esz);
+  const size_t o_gxh = take((size_t)B * Ry * Cx * esz);
+  const size_t nslice = gx_fused_applies(h->bf16, B, (int)Cx, (int)Cy)
+                            ? 0
+                            : (size_t)gemm_ws_slices(h->bf16, false, B * (int)Ry, (int)Cx, (int)Cy);
+  const size_t part_floats = nslice * B * Ry * Cx;
+  const size_t o_part = take(part_floats * sizeof(float));
+  if (off > STATIC_SCRATCH_BYTES) return INSTANT_E_SHAPE;
+  char* base = (char*)h->scratch;
+  const BwdScratch sc{base + o_pgy, base + o_qgy, base + o_gxh, (float*)(base + o_part), part_floats};
+  return run_backward(h, xhat, gy, w, B, gw, gx, sc, S(stream));
 }
 
 INSTANT_API instant_status instant_query(instant_layer* h, instant_info* out) {
