@@ -235,10 +235,11 @@ class InstantLayer:
         self.close()
         return False
 
-    def __del__(self):
-        # during interpreter finalization the HIP runtime may be going away: leave the
-        # small host handle to the process exit (the atexit hook has closed it already)
-        if sys.is_finalizing():
+    def __del__(self, _finalizing=sys.is_finalizing):
+        # during interpreter finalization the HIP runtime may be going away (and this
+        # module's globals may already be cleared): leave the small host handle to the process
+        # exit (the atexit hook has closed it already)
+        if getattr(self, "h", None) is None or _finalizing():
             return
         self.close()
 

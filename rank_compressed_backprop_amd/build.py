@@ -18,7 +18,8 @@ INCLUDE = os.path.join(REPO, "include")
 OUT = os.path.join(HERE, "libinstant.so")
 OBJDIR = os.path.join(REPO, "_build")
 
-SOURCES = ["kernels_proj.hip", "kernels_hot.hip", "kernels_calib.hip", "kernels_eig.hip", "instant_api.cpp"]
+SOURCES = ["kernels_proj.hip", "kernels_hot.hip", "kernels_gemm.hip", "kernels_calib.hip", "kernels_eig.hip",
+           "instant_api.cpp"]
 
 COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-fvisibility=hidden",
           "-I" + INCLUDE, "-I" + CSRC]

@@ -109,11 +109,21 @@ Layout layout_of(const instant_config* c) {
     l.PQ[b] = take((size_t)2 * c->R_max * l.ldL * esz);
     l.Qt[b] = take(L * LD_QT * esz);
   }
-  // float32 K-slice partials of g_hat_x = (Q gy) w when w is too large for L2 (M = B Ry rows)
+  // float32 K-slice partials of the unfused path's GEMMs (they run one after the other):
+  // g_hat_x = (Q gy) w read once over K slices when w is too large for L2 (M = B Ry rows), or
+  // either GEMM on LDS tiles when its K is split
   {
     size_t need = 0;
+    const bool bf = c->dtype == INSTANT_BF16;
     for (int m = 1; m <= c->B_max * c->R_max; ++m)
-      need = std::max(need, (size_t)gemm_ws_slices(c->dtype == INSTANT_BF16, false, m, c->Cx, c->Cy) * m * c->Cx);
+      need = std::max(need, (size_t)gemm_ws_slices(bf, false, m, c->Cx, c->Cy) * m * c->Cx);
+    if (bf)
+      for (int m = 1; m <= c->B_max * c->R_max; ++m) {
+        if (gemm_tiled_applies(true, c->Cy, c->Cx, m))  // g_w, K = B Rx
+          need = std::max(need, gemm_tiled_part_floats(c->Cy, c->Cx, m));
+        if (!gemm_ws_slices(true, false, m, c->Cx, c->Cy) && gemm_tiled_applies(false, m, c->Cx, c->Cy))
+          need = std::max(need, gemm_tiled_part_floats(m, c->Cx, c->Cy));  // g_hat_x, M = B Ry
+      }
     l.gpart_floats = need;
     l.gpart = take(need * sizeof(float));
   }
@@ -448,13 +458,24 @@ instant_status run_backward(instant_layer* h, const void* xhat, const void* gy, 
       e = launch_bwd_tail(h->bf16, sc.Qgy, w, h->Qt(a), LD_QT, B, Ry, L, Cy, Cx, gx, sc.Pgy, xhat, gw, B * Rx,
                           h->ncu, st);
   } else {
-    // g_w = sum_b (P gy_b)^T x_hat_b: M = Cy, N = Cx, K = B * Rx
+    const void* zpad = h->ws + h->lay.zpad;
+    // g_w = sum_b (P gy_b)^T x_hat_b: M = Cy, N = Cx, K = B * Rx (LDS-staged tiles or
+    // register-blocked, whichever is faster for the shapes)
     if (e == hipSuccess)
-      e = launch_gemm(h->bf16, true, sc.Pgy, Cy, 0, xhat, Cx, 0, gw, Cx, 0, 1, Cy, Cx, B * Rx, st);
-    // g_hat_x = (Q gy) w: M = B * Ry, N = Cx, K = Cy
-    if (e == hipSuccess)
-      e = launch_gemm(h->bf16, false, sc.Qgy, Cy, 0, w, Cx, 0, sc.gxh, Cx, 0, 1, B * Ry, Cx, Cy, st, sc.gpart,
-                      sc.gpart_floats, h->ws + h->lay.zpad);
+      e = h->bf16 && gemm_tiled_applies(true, Cy, Cx, B * Rx)
+              ? launch_gemm_tiled(true, sc.Pgy, Cy, xhat, Cx, gw, Cx, Cy, Cx, B * Rx, sc.gpart, sc.gpart_floats,
+                                  zpad, st)
+              : launch_gemm(h->bf16, true, sc.Pgy, Cy, 0, xhat, Cx, 0, gw, Cx, 0, 1, Cy, Cx, B * Rx, st);
+    // g_hat_x = (Q gy) w: M = B * Ry, N = Cx, K = Cy; a w too large for L2 is read once over
+    // K slices, otherwise LDS-staged tiles or register-blocked as for g_w
+    if (e == hipSuccess) {
+      if (h->bf16 && !gemm_ws_slices(true, false, B * Ry, Cx, Cy) && gemm_tiled_applies(false, B * Ry, Cx, Cy))
+        e = launch_gemm_tiled(false, sc.Qgy, Cy, w, Cx, sc.gxh, Cx, B * Ry, Cx, Cy, sc.gpart, sc.gpart_floats, zpad,
+                              st);
+      else
+        e = launch_gemm(h->bf16, false, sc.Qgy, Cy, 0, w, Cx, 0, sc.gxh, Cx, 0, 1, B * Ry, Cx, Cy, st, sc.gpart,
+                        sc.gpart_floats, zpad);
+    }
     // g_x_b = Q^T g_hat_x_b
     if (e == hipSuccess) e = launch_expand(h->bf16, h->Qt(a), LD_QT, sc.gxh, B, Ry, L, Cx, gx, st);
   }
@@ -491,10 +512,17 @@ INSTANT_API instant_status instant_backward_static(instant_layer* h, const void*
   const size_t o_pgy = take((size_t)B * Rx * Cy * esz);
   const size_t o_qgy = take((size_t)B * Ry * Cy * esz);
   const size_t o_gxh = take((size_t)B * Ry * Cx * esz);
-  const size_t nslice = gx_fused_applies(h->bf16, B, (int)Cx, (int)Cy)
-                            ? 0
-                            : (size_t)gemm_ws_slices(h->bf16, false, B * (int)Ry, (int)Cx, (int)Cy);
-  const size_t part_floats = nslice * B * Ry * Cx;
+  size_t part_floats = 0;
+  if (!gx_fused_applies(h->bf16, B, (int)Cx, (int)Cy)) {
+    const int ws = gemm_ws_slices(h->bf16, false, B * (int)Ry, (int)Cx, (int)Cy);
+    part_floats = (size_t)ws * B * Ry * Cx;
+    if (h->bf16) {
+      if (gemm_tiled_applies(true, (int)Cy, (int)Cx, B * (int)Rx))
+        part_floats = std::max(part_floats, gemm_tiled_part_floats((int)Cy, (int)Cx, B * (int)Rx));
+      if (!ws && gemm_tiled_applies(false, B * (int)Ry, (int)Cx, (int)Cy))
+        part_floats = std::max(part_floats, gemm_tiled_part_floats(B * (int)Ry, (int)Cx, (int)Cy));
+    }
+  }
   const size_t o_part = take(part_floats * sizeof(float));
   if (off > STATIC_SCRATCH_BYTES) return INSTANT_E_SHAPE;
   char* base = (char*)h->scratch;

@@ -24,6 +24,18 @@ hipError_t launch_gemm(bool bf16_io, bool a_trans, const void* A, int lda, size_
 // K slices (0: not used) of that path for these shapes; it needs S * M * N floats of part.
 int gemm_ws_slices(bool bf16_io, bool a_trans, int M, int N, int K);
 
+// bf16 C[M][N] = sum_k A(m,k) B[k][n] on LDS-staged 128 x 128 tiles (kernels_gemm.hip).
+// a_kmajor: A stored [K][lda] (m contiguous), else [M][lda]; B stored [K][ldb]. N % 8 == 0,
+// and M % 8 == 0 (k-major A) or K % 8 == 0 (m-major A). When K is split into S > 1 slices
+// (gemm_tiled_slices) the float32 partials need gemm_tiled_part_floats(M, N, K) floats of
+// part. zpad: 16 zero bytes in device memory.
+int gemm_tiled_slices(int M, int N, int K);
+// Whether the tiled kernel is the faster choice for these shapes (and supports them).
+bool gemm_tiled_applies(bool a_kmajor, int M, int N, int K);
+size_t gemm_tiled_part_floats(int M, int N, int K);
+hipError_t launch_gemm_tiled(bool a_kmajor, const void* A, int lda, const void* Bm, int ldb, void* Cm, int ldc, int M,
+                             int N, int K, float* part, size_t part_floats, const void* zpad, hipStream_t st);
+
 // Out[b][l][c] = sum_{r<R} At[l][r] Bz[b][r][c]; At: [L][ldA], zero beyond column R.
 hipError_t launch_expand(bool bf16_io, const void* At, int ldA, const void* Bz, int B, int R, int L, int C,
                          void* out, hipStream_t st);

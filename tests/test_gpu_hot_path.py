@@ -80,6 +80,11 @@ RAGGED = [
     # w (1544 x 11008, 34 MB) too large for L2: g_hat_x reads it once over K slices, with a
     # partial last column strip and a row count (3 * 23) that fills no whole tile
     ("bf16", 3, 70, 1544, 11008, 19, 23),
+    # LDS-tiled g_w with K split in two slices (K = 960) and ragged M (1800) and N (1000)
+    ("bf16", 32, 40, 1000, 1800, 30, 30),
+    # LDS-tiled g_hat_x (270 tiles) with ragged M (40 * 29), N (3400) and a partial last stage
+    # (K = 1032); LDS-tiled g_w unsplit with a ragged K (520)
+    ("bf16", 40, 40, 3400, 1032, 13, 29),
     # fused g_x with two samples stacked per block (2 * Ry <= 16) and an odd batch: the last
     # group holds one sample
     ("bf16", 5, 64, 136, 264, 7, 7),
