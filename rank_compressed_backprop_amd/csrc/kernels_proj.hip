@@ -102,11 +102,11 @@ __global__ __launch_bounds__(NW * WAVE) void proj_kernel(const T* __restrict__ A
   }
 }
 
-template <class T, int MT, int NW, int SW>
+template <class T, int MT, int NW, int SW,
+          int U = NW >= 8 ? (MT <= 2 ? 2 : 1) : (MT <= 2 ? 4 : (MT <= 5 ? 2 : 1))>
 static hipError_t proj_cfg(const void* A, int ldA, int M, int M0, const void* X, int B, int L, int C, void* out0,
                            void* out1, hipStream_t st) {
-  // loads in flight vs registers; with eight waves a strip is already split finely
-  constexpr int U = NW >= 8 ? (MT <= 2 ? 2 : 1) : (MT <= 2 ? 4 : (MT <= 5 ? 2 : 1));
+  // (U: loads in flight vs registers; with eight waves a strip is already split finely)
   dim3 grid((C + 16 * SW - 1) / (16 * SW), B);
   hipLaunchKernelGGL((proj_kernel<T, MT, NW, U, SW>), grid, dim3(NW * WAVE), 0, st, (const T*)A, ldA, M, M0,
                      (const T*)X, L, C, (T*)out0, (T*)out1);
@@ -117,6 +117,15 @@ template <class T, int MT>
 static hipError_t proj_mt(const void* A, int ldA, int M, int M0, const void* X, int B, int L, int C, void* out0,
                           void* out1, hipStream_t st) {
   const int nsteps = (L + MM<T>::KSTEP - 1) / MM<T>::KSTEP;
+  // A token axis of one or two k-steps (EfficientFormer's 49 tokens): one wave per block and
+  // sample strip, all k-steps in one wave and no reduction across waves; the blocks are small
+  // enough to keep every compute unit busy (measured on gfx950 at B = 128, L = 49: 27.0 ->
+  // 15.2 us for [P; Q] g_y with C = 1792, 20.4 -> 9.4 us for x_hat with C = 1792, 6.1 -> 4.7 us
+  // with C = 448, against two waves splitting the two k-steps)
+  // (float32 reaches two k-steps only with L <= 32, so M = Rx + Ry <= 64: MT <= 4)
+  if constexpr (sizeof(T) == 2 || MT <= 4) {
+    if (nsteps <= 2) return proj_cfg<T, MT, 1, 8, 2>(A, ldA, M, M0, X, B, L, C, out0, out1, st);
+  }
   // eight waves per strip keep the most loads in flight per compute unit (measured on
   // gfx950 at B=32, L=512, C=768); narrower strips when 128-column strips would leave
   // compute units idle and the token axis is short
