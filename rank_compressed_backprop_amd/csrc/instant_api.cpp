@@ -76,7 +76,7 @@ bool config_ok(const instant_config* c) {
 }
 
 struct Layout {
-  size_t SX, SG, zpad, part, part_x_tiles, eig, sig_x, sig_g, info, rank, P32[2], Q32[2], PQ[2], Qt[2], Pgy, Qgy,
+  size_t SX, SG, zpad, part, part_x_floats, eig, sig_x, sig_g, info, rank, P32[2], Q32[2], PQ[2], Qt[2], Pgy, Qgy,
       gxh, gpart, gpart_floats, total;
   int ldL;
 };
@@ -95,9 +95,18 @@ Layout layout_of(const instant_config* c) {
   l.SX = take(L * L * sizeof(double));
   l.SG = take(L * L * sizeof(double));
   l.zpad = take(256);
-  l.part_x_tiles = (size_t)syrk_split_max(*c, c->Cx) * syrk_tiles(c->L);
-  l.part = take((l.part_x_tiles + (size_t)syrk_split_max(*c, c->Cy) * syrk_tiles(c->L)) * SYRK_TILE * SYRK_TILE *
-                sizeof(float));
+  {
+    // float32 partials of the statistics, one region per statistic: split K slices of the
+    // 128 x 128 tiles, or the per-block partials of the one-tile path at L <= 64
+    auto side = [&](int C) {
+      size_t f = (size_t)syrk_split_max(*c, C) * syrk_tiles(c->L) * SYRK_TILE * SYRK_TILE;
+      if (c->L <= 64)
+        for (int b = 1; b <= c->B_max; ++b) f = std::max(f, syrk_small_part_floats(c->dtype == INSTANT_BF16, b, C));
+      return f;
+    };
+    l.part_x_floats = side(c->Cx);
+    l.part = take((l.part_x_floats + side(c->Cy)) * sizeof(float));
+  }
   l.eig = take(eig_workspace_bytes(c->L));
   l.sig_x = take(L * sizeof(float));
   l.sig_g = take(L * sizeof(float));
@@ -189,9 +198,7 @@ struct instant_layer {
   double* SX() const { return (double*)(ws + lay.SX); }
   double* SG() const { return (double*)(ws + lay.SG); }
   // partial tiles of the statistics' split reduction, one region per statistic
-  float* part(int side) const {
-    return (float*)(ws + lay.part) + (side ? lay.part_x_tiles * SYRK_TILE * SYRK_TILE : 0);
-  }
+  float* part(int side) const { return (float*)(ws + lay.part) + (side ? lay.part_x_floats : 0); }
   int* info_dev() const { return (int*)(ws + lay.info); }
   int* rank_dev() const { return (int*)(ws + lay.rank); }
   float* P32(int b) const { return (float*)(ws + lay.P32[b]); }

@@ -203,8 +203,140 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(SyrkSide s0, SyrkSide 
   else S[(size_t)i * L + j] += acc;
 }
 
+// ---------------------------------------------------------------- statistics, L <= 64
+// A token axis of at most 64 (EfficientFormer's 49 tokens) fills one 64 x 64 tile; only its
+// ten upper 16 x 16 tiles are computed. The (sample, channel) reduction is cut into k-steps;
+// each wave takes SMALL_KPW consecutive ones, loads all of them at once (rows beyond L read as
+// zero) and multiplies: in S = sum X X^T the same fragments serve as both operands. The four
+// waves of a block are summed through LDS in wave order into one float32 partial per block,
+// [part][10 tiles][4][64] in fragment order; syrk_small_reduce_kernel adds the partials
+// into the float64 sums in a fixed order.
+constexpr int SMALL_KPW = 8;
+constexpr int SMALL_TILES = 10;  // 16 x 16 tiles (t, u), t <= u < 4
+constexpr int SMALL_PART = SMALL_TILES * 4 * WAVE;
+
+__device__ __forceinline__ void small_tile(int k, int& t, int& u) {
+  // (0,0) (0,1) (0,2) (0,3) (1,1) (1,2) (1,3) (2,2) (2,3) (3,3)
+  t = k < 4 ? 0 : (k < 7 ? 1 : (k < 9 ? 2 : 3));
+  const int first = t == 0 ? 0 : (t == 1 ? 4 : (t == 2 ? 7 : 9));
+  u = t + (k - first);
+}
+
+template <class T>
+__global__ __launch_bounds__(256) void syrk_small_kernel(SyrkSide s0, SyrkSide s1, int nb0, int B, int L) {
+  typedef MM<T> mm;
+  typedef typename mm::frag frag;
+  __shared__ float red[4][SMALL_TILES][4][WAVE];
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const bool second = (int)blockIdx.x >= nb0;
+  const int p = second ? blockIdx.x - nb0 : blockIdx.x;
+  const T* __restrict__ X = (const T*)(second ? s1.X : s0.X);
+  const int C = second ? s1.C : s0.C;
+  float* __restrict__ part = second ? s1.part : s0.part;
+  const int nks = (C + mm::KSTEP - 1) / mm::KSTEP;
+  const int total = B * nks;
+  const int q0 = (p * 4 + wave) * SMALL_KPW;
+  frag f[SMALL_KPW][4];
+#pragma unroll
+  for (int i = 0; i < SMALL_KPW; ++i) {
+    const int q = q0 + i;
+    const int b = q / nks;
+    const int c0 = (q - b * nks) * mm::KSTEP + mm::G * (lane >> 4);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int l = 16 * t + (lane & 15);
+      f[i][t] = load_frag<T>(X + ((size_t)b * L + l) * C + c0, q < total && l < L && c0 < C);
+    }
+  }
+  f32x4 acc[SMALL_TILES];
+#pragma unroll
+  for (int k = 0; k < SMALL_TILES; ++k) acc[k] = zero4();
+#pragma unroll
+  for (int i = 0; i < SMALL_KPW; ++i)
+#pragma unroll
+    for (int k = 0; k < SMALL_TILES; ++k) {
+      int t, u;
+      small_tile(k, t, u);
+      acc[k] = mm::mma(f[i][t], f[i][u], acc[k]);
+    }
+#pragma unroll
+  for (int k = 0; k < SMALL_TILES; ++k)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave][k][v][lane] = acc[k][v];
+  __syncthreads();
+  float* __restrict__ out = part + (size_t)p * SMALL_PART;
+  const float* r = &red[0][0][0][0];
+  for (int e = threadIdx.x; e < SMALL_PART; e += 256)
+    out[e] = ((r[e] + r[SMALL_PART + e]) + r[2 * SMALL_PART + e]) + r[3 * SMALL_PART + e];
+}
+
+// S[i][j] (+)= sum_p part[p][e] (float64), e the fragment-order index of (i, j). Eight
+// threads share an entry: thread g sums the parts of its fixed range [g np / 8, (g+1) np / 8)
+// in order, four loads in flight, and the eight range sums are added in range order.
+constexpr int SMALL_RED_GROUPS = 8;
+constexpr int SMALL_RED_ENTRIES = 256 / SMALL_RED_GROUPS;  // entries per block
+__global__ __launch_bounds__(256) void syrk_small_reduce_kernel(SyrkSide s0, SyrkSide s1, int np0, int np1, int L) {
+  __shared__ double red[SMALL_RED_GROUPS][SMALL_RED_ENTRIES];
+  const SyrkSide& sd = blockIdx.y ? s1 : s0;
+  const int np = blockIdx.y ? np1 : np0;
+  const int g = threadIdx.x / SMALL_RED_ENTRIES, j = threadIdx.x % SMALL_RED_ENTRIES;
+  const int e = blockIdx.x * SMALL_RED_ENTRIES + j;  // < SMALL_PART
+  const int qb = (int)((long)np * g / SMALL_RED_GROUPS), qe = (int)((long)np * (g + 1) / SMALL_RED_GROUPS);
+  const float* __restrict__ pp = sd.part + e;
+  double acc = 0.0;
+  int q = qb;
+  for (; q + 4 <= qe; q += 4) {
+    const float v0 = pp[(size_t)(q + 0) * SMALL_PART], v1 = pp[(size_t)(q + 1) * SMALL_PART];
+    const float v2 = pp[(size_t)(q + 2) * SMALL_PART], v3 = pp[(size_t)(q + 3) * SMALL_PART];
+    acc += (double)v0;
+    acc += (double)v1;
+    acc += (double)v2;
+    acc += (double)v3;
+  }
+  for (; q < qe; ++q) acc += (double)pp[(size_t)q * SMALL_PART];
+  red[g][j] = acc;
+  __syncthreads();
+  if (g != 0) return;
+  double sum = red[0][j];
+#pragma unroll
+  for (int h = 1; h < SMALL_RED_GROUPS; ++h) sum += red[h][j];
+  int t, u;
+  small_tile(e >> 8, t, u);
+  const int v = (e >> 6) & 3, lane = e & 63;
+  const int i = 16 * t + 4 * (lane >> 4) + v, jj = 16 * u + (lane & 15);
+  if (i >= L || jj >= L) return;
+  double* __restrict__ S = sd.S;
+  if (sd.overwrite) S[(size_t)i * L + jj] = sum;
+  else S[(size_t)i * L + jj] += sum;
+}
+
+int syrk_small_parts(bool bf16_io, int B, int C) {
+  const int kstep = bf16_io ? 32 : 16;
+  const long total = (long)B * ((C + kstep - 1) / kstep);
+  return (int)((total + 4 * SMALL_KPW - 1) / (4 * SMALL_KPW));
+}
+
+size_t syrk_small_part_floats(bool bf16_io, int B, int C) {
+  return (size_t)syrk_small_parts(bf16_io, B, C) * SMALL_PART;
+}
+
+template <class T>
+static hipError_t syrk_small_t(const SyrkSide* sides, int nsides, int B, int L, hipStream_t st) {
+  const bool bf = sizeof(T) == 2;
+  const SyrkSide s0 = sides[0];
+  const SyrkSide s1 = nsides > 1 ? sides[1] : SyrkSide{nullptr, 0, 0, nullptr, nullptr, 0};
+  const int np0 = syrk_small_parts(bf, B, s0.C), np1 = nsides > 1 ? syrk_small_parts(bf, B, s1.C) : 0;
+  hipLaunchKernelGGL(syrk_small_kernel<T>, dim3(np0 + np1), dim3(256), 0, st, s0, s1, np0, B, L);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(syrk_small_reduce_kernel, dim3(SMALL_PART / SMALL_RED_ENTRIES, nsides), dim3(256), 0, st, s0, s1,
+                     np0, np1, L);
+  return hipGetLastError();
+}
+
 template <class T>
 static hipError_t syrk_t(const SyrkSide* sides, int nsides, int B, int L, const void* zpad, hipStream_t st) {
+  if (L <= 64) return syrk_small_t<T>(sides, nsides, B, L, st);
   const SyrkSide s0 = sides[0];
   const SyrkSide s1 = nsides > 1 ? sides[1] : SyrkSide{nullptr, 0, 0, nullptr, nullptr, 0};
   const int nt = syrk_tiles(L);

@@ -66,6 +66,9 @@ struct SyrkSide {
 hipError_t launch_syrk(bool bf16_io, const SyrkSide* sides, int nsides, int B, int L, const void* zpad,
                        hipStream_t st);
 int syrk_tiles(int L);
+// With L <= 64 the statistics take one 64 x 64 tile and nsplit is not used: a side's partials
+// need syrk_small_part_floats(bf16_io, B, C) floats of its part region.
+size_t syrk_small_part_floats(bool bf16_io, int B, int C);
 
 // Eigen-decomposition of both statistics (C = S * inv_n, float64 upper-triangle sums)
 // by blocked one-sided Jacobi, then truncation, compensation and the float32
