@@ -82,6 +82,8 @@ def parse():
                          "consecutive calibration windows see different statistics; N_cal for llm_mlp, "
                          "whose batches take seconds each to generate)")
     ap.add_argument("--windows", type=int, default=2, help="whole N_t windows timed for the schedule rate")
+    ap.add_argument("--runs", type=int, default=TIMED_RUNS,
+                    help=f"timed runs of {CALLS_PER_RUN} consecutive instant_backward calls (the metric's samples)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--one-stream", action="store_true",
                     help="run the statistics on the main stream too (no overlap with the hot path)")
@@ -279,8 +281,9 @@ def main():
     for r in range(WARM_RUNS):
         run(r)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(TIMED_RUNS)]
-    for r in range(TIMED_RUNS):
+    runs = max(args.runs, 1)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(runs)]
+    for r in range(runs):
         evs[r][0].record(st)
         run(r)
         evs[r][1].record(st)
@@ -363,7 +366,7 @@ def main():
                                f"eps={wl.eps} p={wl.p} N_cal={wl.n_cal} N_t={wl.n_t}",
                    "global_batch": B, "seq_len": L, "parallelism": "single GPU",
                    "value": "B*L / median time of one instant_backward (a5-a8): HIP events around runs of "
-                            f"{CALLS_PER_RUN} consecutive calls on rotating resident batches, {TIMED_RUNS} timed "
+                            f"{CALLS_PER_RUN} consecutive calls on rotating resident batches, {runs} timed "
                             "runs after 20 untimed ones",
                    "step": "ms_per_step: compress + low-rank backward every step; statistics on the first N_cal "
                            "steps of each N_t window; eigen-decomposition + truncation once per window",
@@ -402,7 +405,7 @@ def main():
                                "kernels, one call", "bound": "hbm",
                      "achieved": gbs_bwd_mean, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs_bwd_mean / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name + "/" + ly.name),
-                     "launch_us_mean": t_bwd_mean * 1e6, "calls_timed": TIMED_RUNS * CALLS_PER_RUN,
+                     "launch_us_mean": t_bwd_mean * 1e6, "calls_timed": runs * CALLS_PER_RUN,
                      "algorithmic_bytes_per_call": bytes_bwd},
     }
 
