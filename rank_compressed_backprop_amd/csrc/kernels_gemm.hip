@@ -18,13 +18,13 @@
 // row k0 + s / 4 (+ 4 for the second read) at columns cb(s % 4) .. cb(s % 4) + 3, so lane i
 // ends with the 8 consecutive k of column cb(i / 4) + i % 4: an MFMA operand without register
 // shuffles. An m-major tile (128 rows x 64 k, 128 bytes a row) is read with one 16-byte read
-// per lane. 16-byte chunks are XOR-swizzled by row so both reads run without bank conflicts.
+// per lane. 16-byte chunks are XOR-swizzled by row so the reads avoid bank conflicts.
 //
 // Orientation. The MFMA computes D[n][m] = C[m][n]: the B operand (columns n) takes the
 // first operand slot, A (rows m) the second. A lane then holds D rows 4 q + v (q = lane / 16,
-// v < 4) of one column m; with the column bases cb of the two tiles of a 32-column pair set
-// to 8 a + 4 h (h = 0, 1), those rows are the 8 consecutive columns n = 8 q .. 8 q + 7 of the
-// pair: results leave as 16-byte stores.
+// v < 4) of one column m; with the column bases cb of the two tiles (halves hh = 0, 1) of a
+// 32-column pair set to 8 a + 4 (hh ^ (a % 2)), those rows of the two tiles are the 8
+// consecutive columns n = 8 q .. 8 q + 7 of the pair: results leave as 16-byte stores.
 //
 // Split K: with grid.z = S > 1 every slice writes float32 partials [S][M][N] that a second
 // launch sums in slice order (deterministic).
@@ -45,12 +45,18 @@ constexpr int MMAJ_BYTES = GT * GBK * 2;   // an m-major tile of a stage: 128 ro
 constexpr int STAGE_BYTES = KMAJ_BYTES + 16384;  // B tile, then the A tile (16 KB either way)
 static_assert(MMAJ_BYTES == 16384 && KMAJ_BYTES == 16384, "tile sizes");
 
-// k-major tile: 16-byte chunk c of row r lives at chunk c ^ kswz(r). A transpose read of a
-// 16-lane group touches 4 consecutive rows (s / 4) and, in each, 8 bytes in each of 4
-// consecutive chunks starting at a multiple of 4 (B operand) or 2 chunks (A operand, two
-// lanes a chunk): XOR with 4 (r % 4) moves the rows to disjoint 64-byte quarters of the
-// 256-byte bank sweep, so the 16 reads hit distinct banks.
-__device__ __forceinline__ int kswz(int r) { return 4 * (r & 3); }
+// k-major tiles: 16-byte chunk c of row r lives at chunk c ^ swz(r). The LDS serves a
+// transpose read 16 lanes at a time from a 128-byte bank window (measured on gfx950: a
+// swizzle built for 256-byte windows left half the LDS cycles in bank conflicts). The 16
+// lanes read 4 consecutive rows (r % 4), each at 4 places:
+//   B tiles (pairs of 32 columns, AS = 8): 8 bytes in each of 4 consecutive chunks,
+//     alternating halves (see kmajor_frag); XOR with 0, 1, 4, 5 for r % 4 = 0..3 gives the
+//     rows disjoint (chunk mod 8, half) slots;
+//   A tiles (16 consecutive columns, AS = 4): both halves of 2 consecutive chunks; XOR with
+//     0, 2, 4, 6 gives the rows disjoint chunk pairs mod 8.
+// Both also flip chunk bit 3 for rows 8-15 of each 16, in case two groups share a window.
+__device__ __forceinline__ int kswz_b(int r) { return ((r & 1) | ((r & 2) << 1)) ^ (((r >> 3) & 1) << 3); }
+__device__ __forceinline__ int kswz_a(int r) { return (2 * (r & 3)) ^ (((r >> 3) & 1) << 3); }
 // m-major tile: chunk c of row r at c ^ (r & 7) (8 chunks a row, one 16-byte read per lane).
 __device__ __forceinline__ int mswz(int r) { return r & 7; }
 
@@ -60,18 +66,20 @@ __device__ __forceinline__ bf16x4 tr_read(const unsigned char* p) {
 }
 
 // One MFMA operand from a k-major tile: lane (q = lane / 16, i = lane % 16) receives the 8 k
-// values 32 h + 8 q .. + 7 of column col0 + AS * (i / 4) + i % 4. As a source, lane s
-// addresses row 32 h + 8 q + s / 4 (+ 4 for the second half) at columns col0 + AS * (s % 4)
-// .. + 3. AS = 4 gives the 16 consecutive columns col0 .. col0 + 15; AS = 8 gives one half
-// (col0 = pair base + 4 hh) of a 32-column pair.
-template <int AS>
-__device__ __forceinline__ MM<bf16>::frag kmajor_frag(const unsigned char* tile, int h, int lane, int col0) {
-  const int q = lane >> 4, s = lane & 15;
-  const int col = col0 + AS * (s & 3);
+// values 32 h + 8 q .. + 7 of column cb(i / 4) + i % 4. As a source, lane s addresses row
+// 32 h + 8 q + s / 4 (+ 4 for the second half) at columns cb(s % 4) .. + 3, where
+//   PAIR = false: cb(a) = col0 + 4 a, the 16 consecutive columns col0 .. col0 + 15;
+//   PAIR = true : cb(a) = col0 + 8 a + 4 (hh ^ (a % 2)), half hh of the 32-column pair at col0:
+//                 quad a of the two halves together covers columns col0 + 8 a .. + 7.
+template <bool PAIR>
+__device__ __forceinline__ MM<bf16>::frag kmajor_frag(const unsigned char* tile, int h, int lane, int col0, int hh) {
+  const int q = lane >> 4, s = lane & 15, a = s & 3;
+  const int col = PAIR ? col0 + 8 * a + 4 * (hh ^ (a & 1)) : col0 + 4 * a;
   const int chunk = col >> 3, within = (col & 7) * 2;
   const int r0 = 32 * h + 8 * q + (s >> 2), r1 = r0 + 4;
-  const bf16x4 lo = tr_read(tile + r0 * 256 + 16 * (chunk ^ kswz(r0)) + within);
-  const bf16x4 hi = tr_read(tile + r1 * 256 + 16 * (chunk ^ kswz(r1)) + within);
+  const int w0 = PAIR ? kswz_b(r0) : kswz_a(r0), w1 = PAIR ? kswz_b(r1) : kswz_a(r1);
+  const bf16x4 lo = tr_read(tile + r0 * 256 + 16 * (chunk ^ w0) + within);
+  const bf16x4 hi = tr_read(tile + r1 * 256 + 16 * (chunk ^ w1) + within);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -107,7 +115,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const bf16* __restrict_
 #pragma unroll
     for (int j = 0; j < 4; ++j) {  // B: k-major, 64 rows x 16 chunks, 4 rows per wave-load
       const int r = 16 * j + 4 * wave + (lane >> 4);
-      const int pc = lane & 15, lc = pc ^ kswz(r);
+      const int pc = lane & 15, lc = pc ^ kswz_b(r);
       const int k = k0 + r, n = n0 + 8 * lc;
       const void* src = (k < K && n < N) ? (const void*)(Bm + (size_t)k * ldb + n) : (const void*)zpad;
       lds_dma16(src, st + 1024 * (4 * j + wave));
@@ -117,7 +125,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const bf16* __restrict_
       const void* src;
       if constexpr (A_KM) {  // A: k-major like B
         const int r = 16 * j + 4 * wave + (lane >> 4);
-        const int pc = lane & 15, lc = pc ^ kswz(r);
+        const int pc = lane & 15, lc = pc ^ kswz_a(r);
         const int k = k0 + r, m = m0 + 8 * lc;
         src = (k < K && m < M) ? (const void*)(A + (size_t)k * lda + m) : (const void*)zpad;
       } else {  // A: m-major, 128 rows x 8 chunks, 8 rows per wave-load
@@ -152,12 +160,12 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const bf16* __restrict_
     for (int h = 0; h < 2; ++h) {
       mm::frag bfr[4], afr[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)  // n tiles: two 32-column pairs, halves 4 columns apart
-        bfr[j] = kmajor_frag<8>(st, h, lane, 64 * wn + 32 * (j >> 1) + 4 * (j & 1));
+      for (int j = 0; j < 4; ++j)  // n tiles: the two halves of two 32-column pairs
+        bfr[j] = kmajor_frag<true>(st, h, lane, 64 * wn + 32 * (j >> 1), j & 1);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         if constexpr (A_KM) {
-          afr[mt] = kmajor_frag<4>(ta, h, lane, 64 * wm + 16 * mt);
+          afr[mt] = kmajor_frag<false>(ta, h, lane, 64 * wm + 16 * mt, 0);
         } else {
           const int r = 64 * wm + 16 * mt + l16;
           afr[mt] = *reinterpret_cast<const mm::frag*>(ta + r * 128 + 16 * ((4 * h + q4) ^ mswz(r)));
@@ -170,7 +178,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const bf16* __restrict_
     }
   }
 
-  // lane: column m = m0 + 64 wm + 16 mt + l16 of D, rows n = pair base + 8 q4 + (0..7)
+  // lane: column m = m0 + 64 wm + 16 mt + l16 of D, rows n = pair base + 8 q4 + (0..7): the
+  // first four from half q4 % 2 of the pair, the last four from the other half
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int m = m0 + 64 * wm + 16 * mt + l16;
@@ -180,10 +189,11 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const bf16* __restrict_
       const int n = n0 + 64 * wn + 32 * p + 8 * q4;
       if (n >= N) continue;
       float o[8];
+      const int h0 = q4 & 1;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        o[v] = acc[mt][2 * p][v];
-        o[4 + v] = acc[mt][2 * p + 1][v];
+        o[v] = h0 ? acc[mt][2 * p + 1][v] : acc[mt][2 * p][v];
+        o[4 + v] = h0 ? acc[mt][2 * p][v] : acc[mt][2 * p + 1][v];
       }
       if constexpr (PART) {
         float* dst = part + ((size_t)z * M + m) * N + n;
