@@ -8,10 +8,15 @@
 namespace instant {
 
 // 16 bytes per lane from src straight into LDS at lds_wave + 16 * lane (lds_wave uniform
-// across the wave). Kept out of the kernel body: target builtins there would keep the host
-// pass from emitting the kernel's launch stub.
+// across the wave; the hardware takes it from M0). Written as inline assembly on purpose: the
+// compiler, seeing the intrinsic form write LDS, puts a wait for every outstanding vector
+// load in front of each later LDS read (it cannot tell ring slots apart), which empties the
+// ring at every stage. Here the kernels' own waits (wait_oldest_stage) order the stages. The
+// instruction has no register result; the nop is the wait state a write of M0 needs before
+// a DMA reads it.
 __device__ inline void lds_dma16(const void* src, void* lds_wave) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave, 16, 0, 0);
+  const unsigned lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave;
+  __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
 
 // Workgroup barrier without a memory fence (waits are explicit around it).
