@@ -173,13 +173,15 @@ instant_status instant_backward(instant_layer* h, const void* xhat, const void* 
 /* For callers that cannot allocate device memory at the time of the call (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): instant_backward
  * with its per-call intermediates (P gy, Q gy, g_hat_x and the float32 K-slice partials of
- * g_hat_x, which instant_backward keeps in the handle's workspace) in a static device array
- * of INSTANT_STATIC_SCRATCH_BYTES that the library holds on every device it runs on until
- * the process ends. Same arguments, same kernels and the same results, bit for bit, as
- * instant_backward; no allocation of any kind.
- * The call needs align256(B*Rx*Cy*s) + align256(B*Ry*Cy*s) + align256(B*Ry*Cx*s) bytes,
- * plus the float32 partials when w is too large for L2 (s = bytes per I/O element,
- * align256 = rounded up to 256), and returns E_SHAPE when that exceeds
+ * the g_w and g_hat_x products, which instant_backward keeps in the handle's workspace) in a
+ * static device array of INSTANT_STATIC_SCRATCH_BYTES that the library holds on every device
+ * it runs on until the process ends. Same arguments, same kernels and the same results, bit
+ * for bit, as instant_backward; no allocation of any kind.
+ * The call needs align256(B*Rx*Cy*s) + align256(B*Ry*Cy*s) + align256(B*Ry*Cx*s) bytes
+ * (s = bytes per I/O element, align256 = rounded up to 256), plus, when w does not stay in
+ * L2 for the fused g_x path, 4 bytes per float32 partial of whichever of the two products is
+ * split over K (S slices of its M x N output: g_hat_x's B*Ry x Cx when w is read once in
+ * slices, g_w's Cy x Cx or g_hat_x's on the LDS-tiled GEMM), and returns E_SHAPE when that exceeds
  * INSTANT_STATIC_SCRATCH_BYTES (64 MiB covers B=8, L=2048, Cx=4096, Cy=11008 at Rx=Ry=34).
  * Nothing in the scratch needs to start at zero: every byte read is written earlier in the
  * same call. All calls on one GPU share its array, so calls that overlap on one GPU (other
