@@ -437,7 +437,7 @@ INSTANT_API instant_status instant_compress_fwd(instant_layer* h, const void* x,
   if (h->active < 0) return INSTANT_E_STATE;
   const int a = h->active;
   return hip_ok(launch_proj(h->bf16, h->PQ(a), h->lay.ldL, h->Rx, h->Rx, x, B, h->cfg.L, h->cfg.Cx, xhat, nullptr,
-                            S(stream)));
+                            h->ws + h->lay.zpad, S(stream)));
 }
 
 namespace {
@@ -458,14 +458,14 @@ instant_status run_backward(instant_layer* h, const void* xhat, const void* gy, 
   const int a = h->active;
   const int L = h->cfg.L, Cx = h->cfg.Cx, Cy = h->cfg.Cy, Rx = h->Rx, Ry = h->Ry;
   // [P; Q] gy_b from one pass over gy
-  hipError_t e = launch_proj(h->bf16, h->PQ(a), h->lay.ldL, Rx + Ry, Rx, gy, B, L, Cy, sc.Pgy, sc.Qgy, st);
+  const void* zpad = h->ws + h->lay.zpad;
+  hipError_t e = launch_proj(h->bf16, h->PQ(a), h->lay.ldL, Rx + Ry, Rx, gy, B, L, Cy, sc.Pgy, sc.Qgy, zpad, st);
   if (gx_fused_applies(h->bf16, B, Cx, Cy)) {
     // g_x_b = Q^T ((Q gy_b) w) with w resident in L2, and g_w, in one launch
     if (e == hipSuccess)
       e = launch_bwd_tail(h->bf16, sc.Qgy, w, h->Qt(a), LD_QT, B, Ry, L, Cy, Cx, gx, sc.Pgy, xhat, gw, B * Rx,
                           h->ncu, st);
   } else {
-    const void* zpad = h->ws + h->lay.zpad;
     // g_w = sum_b (P gy_b)^T x_hat_b: M = Cy, N = Cx, K = B * Rx (LDS-staged tiles or
     // register-blocked, whichever is faster for the shapes)
     if (e == hipSuccess)

@@ -10,9 +10,11 @@
 namespace instant {
 
 // Out[b][m][c] = sum_l A[m][l] X[b][l][c]; rows m < M0 to out0 [B][M0][C], the rest
-// to out1 [B][M-M0][C]. A: [M][ldA], zero beyond column L. M <= 128.
+// to out1 [B][M-M0][C]. A: [M][ldA], zero beyond column L, ldA a multiple of 32. M <= 128.
+// zpad: 16 zero bytes in device memory (bf16 inputs stream through LDS reading it in place
+// of out-of-range rows; without it they take the register-blocked kernel).
 hipError_t launch_proj(bool bf16_io, const void* A, int ldA, int M, int M0, const void* X, int B, int L, int C,
-                       void* out0, void* out1, hipStream_t st);
+                       void* out0, void* out1, const void* zpad, hipStream_t st);
 
 // Cm[m][n] = sum_k A(m,k) B[k][n] per batch entry z (pointer strides sA, sB, sC in
 // elements). a_trans: A stored [K][lda] instead of [M][lda]. M, N multiples of 4 / 8.
