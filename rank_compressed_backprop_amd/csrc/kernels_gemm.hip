@@ -8,8 +8,8 @@
 //
 // A 128 x 128 block tile is computed by four waves of 64 x 64 over a K slice. Stages of 64 k
 // go from memory straight to LDS (global_load_lds, 16 bytes per lane) through a ring, so the
-// later stages' loads are in flight while the matrix cores consume the oldest; each wave
-// issues the same loads per stage, so the waits are exact counts.
+// later stages' loads are in flight while the matrix cores consume the oldest; four loader
+// waves issue them, each the same loads per stage, so the waits are exact counts.
 //
 // Operands in LDS: k-major tiles (64 k rows x 128 columns) are read through the gfx950
 // transpose read, m-major tiles (128 rows x 64 k) with one 16-byte read per lane; the layouts
@@ -46,14 +46,19 @@ static_assert(MMAJ_BYTES == 16384 && KMAJ_BYTES == 16384, "tile sizes");
 // C = A . B over k slice blockIdx.z (see the file comment). A_KM: A stored [K][lda]
 // (k-major), else [M][lda]. Grid: (tiles, 1, S) with tiles = ceil(M/128) * ceil(N/128).
 // K % 8 == 0 when A is m-major; N % 8 == 0 and M % 8 == 0 when A is k-major.
-template <bool A_KM, int STG, bool PART>
-__global__ __launch_bounds__(256) void gemm_tiled_kernel(const bf16* __restrict__ A, int lda,
+template <bool A_KM, int STG, bool PART, int NLD>
+__global__ __launch_bounds__(64 * (4 + NLD)) void gemm_tiled_kernel(const bf16* __restrict__ A, int lda,
                                                          const bf16* __restrict__ Bm, int ldb,
                                                          bf16* __restrict__ Cm, int ldc, float* __restrict__ part,
                                                          int M, int N, int K, const bf16* __restrict__ zpad) {
   typedef MM<bf16> mm;
   __shared__ __attribute__((aligned(1024))) unsigned char ring[STG][STAGE_BYTES];
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  // NLD = 4: four more waves only stream the ring (loader li issues what compute wave li
+  // would); NLD = 0: the four compute waves stream it themselves
+  const bool loader = NLD ? wave >= 4 : true;
+  const bool computer = wave < 4;
+  const int li = NLD ? wave - 4 : wave;
   const int mtiles = (M + GT - 1) / GT, ntiles = (N + GT - 1) / GT;
   const int ntile_all = mtiles * ntiles;
   // XCD-aware order: the tiles of one XCD are a contiguous run, m fastest, so they share
@@ -66,33 +71,33 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const bf16* __restrict_
   const int nst = (K + GBK - 1) / GBK;
   const int sb = (int)((long)nst * z / S), se = (int)((long)nst * (z + 1) / S), nq = se - sb;
 
-  // every wave issues 8 DMA loads a stage: 4 for the B tile, 4 for the A tile
+  // every loader wave issues 8 DMA loads a stage: 4 for the B tile, 4 for the A tile
   auto issue = [&](int s, int slot) {
     unsigned char* st = ring[slot];
     const int k0 = s * GBK;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {  // B: k-major, 64 rows x 16 chunks, 4 rows per wave-load
-      const int r = 16 * j + 4 * wave + (lane >> 4);
+      const int r = 16 * j + 4 * li + (lane >> 4);
       const int pc = lane & 15, lc = pc ^ kswz_b(r);
       const int k = k0 + r, n = n0 + 8 * lc;
       const void* src = (k < K && n < N) ? (const void*)(Bm + (size_t)k * ldb + n) : (const void*)zpad;
-      lds_dma16(src, st + 1024 * (4 * j + wave));
+      lds_dma16(src, st + 1024 * (4 * j + li));
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const void* src;
       if constexpr (A_KM) {  // A: k-major like B
-        const int r = 16 * j + 4 * wave + (lane >> 4);
+        const int r = 16 * j + 4 * li + (lane >> 4);
         const int pc = lane & 15, lc = pc ^ kswz_a(r);
         const int k = k0 + r, m = m0 + 8 * lc;
         src = (k < K && m < M) ? (const void*)(A + (size_t)k * lda + m) : (const void*)zpad;
       } else {  // A: m-major, 128 rows x 8 chunks, 8 rows per wave-load
-        const int r = 32 * j + 8 * wave + (lane >> 3);
+        const int r = 32 * j + 8 * li + (lane >> 3);
         const int pc = lane & 7, lc = pc ^ mswz(r);
         const int m = m0 + r, k = k0 + 8 * lc;
         src = (m < M && k < K) ? (const void*)(A + (size_t)m * lda + k) : (const void*)zpad;
       }
-      lds_dma16(src, st + KMAJ_BYTES + 1024 * (4 * j + wave));
+      lds_dma16(src, st + KMAJ_BYTES + 1024 * (4 * j + li));
     }
   };
 
@@ -103,15 +108,19 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const bf16* __restrict_
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
 
+  if (loader) {
 #pragma unroll
-  for (int q = 0; q < STG - 1; ++q)
-    if (q < nq) issue(sb + q, q);
+    for (int q = 0; q < STG - 1; ++q)
+      if (q < nq) issue(sb + q, q);
+  }
   const int q4 = lane >> 4, l16 = lane & 15;
   for (int i = 0; i < nq; ++i) {
+    // (waves that issue no loads pass the count at once; all wait for their LDS reads)
     const int later = (nq - 1 - i) < (STG - 2) ? (nq - 1 - i) : (STG - 2);
     wait_oldest_stage<8, STG - 2>(later);
     bare_barrier();  // stage i has landed for every wave; the slot refilled next is free
-    if (i + STG - 1 < nq) issue(sb + i + STG - 1, (i + STG - 1) % STG);
+    if (loader && i + STG - 1 < nq) issue(sb + i + STG - 1, (i + STG - 1) % STG);
+    if (!computer) continue;
     const unsigned char* st = ring[i % STG];
     const unsigned char* ta = st + KMAJ_BYTES;
 #pragma unroll
@@ -136,6 +145,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const bf16* __restrict_
     }
   }
 
+  if (!computer) return;
   // lane: column m = m0 + 64 wm + 16 mt + l16 of D, rows n = pair base + 8 q4 + (0..7): the
   // first four from half q4 % 2 of the pair, the last four from the other half
 #pragma unroll
@@ -187,33 +197,40 @@ __global__ __launch_bounds__(256) void gemm_tiled_reduce_kernel(const float* __r
   }
 }
 
-constexpr int GEMM_TILED_STAGES = 2;  // a 64 KB ring: two blocks share a compute unit
+// Four waves compute, four more only stream the ring (a compute wave that issued its own
+// eight loads a stage spent 750 of its 2000 clocks a stage issuing them, per-phase clock
+// stamps on gfx950; the data had landed long before it waited for them). With loader waves
+// one block fits a compute unit (146 registers a lane), so the ring may be deeper: four
+// stages once a slice is long or the tiles alone fill the chip, two otherwise (measured on
+// gfx950: EfficientFormer g_w 24.3 -> 19.2 us, BERT FFN g_w 10.8 -> 8.0 us, EfficientFormer
+// up g_hat_x 29.1 -> 18.3 us unsplit).
+constexpr int GEMM_TILED_LOADERS = 4;
 
 int gemm_tiled_slices(int M, int N, int K) {
   const long tiles = (long)((M + GT - 1) / GT) * ((N + GT - 1) / GT);
   const int nst = (K + GBK - 1) / GBK;
-  // Split K while the blocks still fit two to a compute unit and every slice keeps >= 7
+  // Split K while the blocks still fit one to a compute unit and every slice keeps >= 8
   // stages: the partials' write and re-read only pay off against a long K (measured on
-  // gfx950: EfficientFormer g_w, 56 tiles, K = 3712: 60 / 36 / 25 / 24 us unsplit / 2 / 4 / 8
-  // slices with the reduction; BERT FFN g_w, 144 tiles, K = 448: 9.1 us unsplit, 20.6 us
-  // in two slices).
+  // gfx950 with loader waves and four stages: EfficientFormer g_w, 56 tiles, K = 3712: 32.4 /
+  // 23.6 / 19.2 / 26.9 us unsplit / 2 / 4 / 8 slices with the reduction; BERT FFN g_w, 144
+  // tiles, K = 448: 8.0 us unsplit, 22 us in two slices).
   int S = 1;
-  while (tiles * 2 * S <= 512 && S < 16 && nst / (2 * S) >= 7) S *= 2;
+  while (tiles * 2 * S <= 256 && S < 16 && nst / (2 * S) >= 8) S *= 2;
   return S;
 }
 
 bool gemm_tiled_applies(bool a_kmajor, int M, int N, int K) {
   const long tiles = (long)((M + GT - 1) / GT) * ((N + GT - 1) / GT);
   if (N % 8 || (a_kmajor ? M % 8 : K % 8)) return false;
-  // (measured on gfx950 against the register-blocked GEMM of kernels_hot.hip)
-  // g_w (k-major A): ahead wherever the output is not huge (EfficientFormer 39 -> 24 us, BERT
-  // FFN 11.8 -> 9.1 us); with >= 2048 tiles and a short K (LLM MLP, 2752 tiles, K = 272) the
-  // register-blocked kernel's 44 us beat 59 us.
+  // (measured on gfx950 against the register-blocked GEMM of kernels_hot.hip, same run)
+  // g_w (k-major A): ahead wherever the output is not huge (EfficientFormer 34.1 -> 19.5 us
+  // with the reduction, BERT FFN 10.5 -> 7.9 us); with >= 2048 tiles and a short K (LLM MLP,
+  // 2752 tiles, K = 272) the register-blocked kernel's 43.7 us beat 67.4 us.
   if (a_kmajor) return tiles < 2048;
   // g_hat_x (m-major A, the weight as B): ahead once the tiles alone cover the compute units
-  // (EfficientFormer down, 406 tiles: 30.4 -> 13.3 us); with fewer tiles the eight-wave
-  // K-splitting blocks of the register-blocked kernel win (EfficientFormer up 17.3 against
-  // 23.4 us, BERT FFN 9-14 against 13-17 us).
+  // (EfficientFormer down, 406 tiles: 30.3 -> 15.1 us); with fewer tiles the eight-wave
+  // K-splitting blocks of the register-blocked kernel win (EfficientFormer up 17.4 against
+  // 19.3 us, BERT FFN 8.5-13.3 against 10.4-15.6 us).
   return tiles >= 256;
 }
 
@@ -229,17 +246,23 @@ hipError_t launch_gemm_tiled(bool a_kmajor, const void* A, int lda, const void* 
   if (S > 1 && (!part || (size_t)S * M * N > part_floats)) return hipErrorInvalidValue;
   const unsigned tiles = (unsigned)(((M + GT - 1) / GT) * ((N + GT - 1) / GT));
   const dim3 grid(tiles, 1, S);
-  constexpr int STG = GEMM_TILED_STAGES;
-#define GT_LAUNCH(AK, PT)                                                                                           \
-  hipLaunchKernelGGL((gemm_tiled_kernel<AK, STG, PT>), grid, dim3(256), 0, st, (const bf16*)A, lda,               \
+  const int nq = (K + GBK - 1) / GBK / S;  // stages of a slice (at least)
+  const bool deep = nq >= 12 || tiles >= 256;
+  constexpr int NLD = GEMM_TILED_LOADERS;
+#define GT_LAUNCH(AK, STG, PT)                                                                                      \
+  hipLaunchKernelGGL((gemm_tiled_kernel<AK, STG, PT, NLD>), grid, dim3(64 * (4 + NLD)), 0, st, (const bf16*)A, lda, \
                      (const bf16*)Bm, ldb, (bf16*)Cm, ldc, part, M, N, K, (const bf16*)zpad)
+#define GT_STAGES(AK, PT)          \
+  if (deep) GT_LAUNCH(AK, 4, PT);  \
+  else GT_LAUNCH(AK, 2, PT);
   if (a_kmajor) {
-    if (S > 1) GT_LAUNCH(true, true);
-    else GT_LAUNCH(true, false);
+    if (S > 1) { GT_STAGES(true, true) }
+    else { GT_STAGES(true, false) }
   } else {
-    if (S > 1) GT_LAUNCH(false, true);
-    else GT_LAUNCH(false, false);
+    if (S > 1) { GT_STAGES(false, true) }
+    else { GT_STAGES(false, false) }
   }
+#undef GT_STAGES
 #undef GT_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
