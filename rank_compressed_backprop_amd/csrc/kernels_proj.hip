@@ -152,21 +152,26 @@ static hipError_t proj_mt(const void* A, int ldA, int M, int M0, const void* X, 
 // The same product for bf16 inputs. Block (128-column strip, sample): stages of 64 tokens x
 // 128 columns of X (16 KB, k-major) and the matching 64 columns of every row of A (MA rows of
 // 128 bytes, m-major) go from memory straight to LDS (global_load_lds) through a PROJ_STAGES
-// deep ring; each of the four waves owns 32 columns and all the row tiles, reading X
+// deep ring; each of the four compute waves owns 32 columns and all the row tiles, reading X
 // fragments with the transpose read and A fragments with 16-byte reads (lds_tiles.hpp), and
 // accumulates over every token itself: no cross-wave reduction. Against the register-blocked
 // kernel, whose loads wait in registers beside 16 * MT * SW accumulators, the ring keeps three
 // stages of X in flight whatever the number of rows (measured on gfx950, bit-identical outputs:
 // LLM MLP [P; Q] g_y, 68 rows, 99.7 -> 72.3 us; x_hat, 34 rows, 32.5 -> 27.0 us; BERT FFN
 // [P; Q] g_y, 28 rows, 27.0 -> 19.5 us; attention [P; Q] g_y, 16 rows, 7.1 -> 6.1 us).
-// Every wave issues 4 + MA / 32 loads a stage (rows and tokens out of range read the zero pad),
-// so its waits are exact counts. The MFMA takes the X operand first: a lane then holds 8
-// consecutive columns of one output row (the pair layout of kmajor_frag), stored as 16 bytes.
-// Needs C % 8 == 0 (16-byte rows); A zero from column L up to ldA >= the next multiple of 8.
+// With two or more row tiles, four more waves only stream the ring: each issues the 4 + MA / 32
+// loads of a stage that one compute wave would (rows and tokens out of range read the zero
+// pad), so the waits are exact counts, and the compute waves do not stall on issuing them
+// (measured on gfx950, same box: LLM MLP backward 204.1 -> 202.0 us, BERT FFN 52.3 -> 51.8
+// us; the kernel alone at the LLM size 81.0 -> 70.7 us). With one row tile the compute waves
+// stream it themselves (attention backward 17.09 us against 17.21 us with loaders). The MFMA
+// takes the X operand first: a lane then holds 8 consecutive columns of one output row (the
+// pair layout of kmajor_frag), stored as 16 bytes. Needs C % 8 == 0 (16-byte rows); A zero from
+// column L up to ldA >= the next multiple of 8.
 constexpr int PROJ_STAGES = 4;
 
-template <int MTL, int MA, int STG>
-__global__ __launch_bounds__(256) void proj_lds_kernel(const bf16* __restrict__ A, int ldA, int M, int M0,
+template <int MTL, int MA, int STG, int NLD>
+__global__ __launch_bounds__(64 * (4 + NLD)) void proj_lds_kernel(const bf16* __restrict__ A, int ldA, int M, int M0,
                                                        const bf16* __restrict__ X, int L, int C,
                                                        bf16* __restrict__ out0, bf16* __restrict__ out1,
                                                        const bf16* __restrict__ zpad) {
@@ -177,6 +182,11 @@ __global__ __launch_bounds__(256) void proj_lds_kernel(const bf16* __restrict__ 
   static_assert(MA % 32 == 0 && 16 * MTL <= MA && LDPS * (STG - 2) <= 63, "A rows, vmcnt range");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[STG][STAGE];
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  // NLD = 4: four more waves only stream the ring (loader li issues what compute wave li
+  // would); NLD = 0: the four compute waves stream it themselves
+  const bool loader = NLD ? wave >= 4 : true;
+  const bool computer = wave < 4;
+  const int li = NLD ? wave - 4 : wave;
   const int n0 = blockIdx.x * 128, b = blockIdx.y;
   const bf16* __restrict__ Xb = X + (size_t)b * L * C;
   const int nq = (L + 63) / 64;
@@ -185,33 +195,37 @@ __global__ __launch_bounds__(256) void proj_lds_kernel(const bf16* __restrict__ 
     const int k0 = 64 * s;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {  // X: rows 16 j + 4 wave + lane / 16, 16 chunks a row
-      const int r = 16 * j + 4 * wave + (lane >> 4);
+      const int r = 16 * j + 4 * li + (lane >> 4);
       const int lc = (lane & 15) ^ kswz_b(r);
       const int k = k0 + r, n = n0 + 8 * lc;
       lds_dma16((k < L && n < C) ? (const void*)(Xb + (size_t)k * C + n) : (const void*)zpad,
-                st + 1024 * (4 * j + wave));
+                st + 1024 * (4 * j + li));
     }
 #pragma unroll
     for (int j = 0; j < MA / 32; ++j) {  // A: rows 32 j + 8 wave + lane / 8, 8 chunks a row
-      const int r = 32 * j + 8 * wave + (lane >> 3);
+      const int r = 32 * j + 8 * li + (lane >> 3);
       const int lc = (lane & 7) ^ mswz(r);
       const int kk = k0 + 8 * lc;
       lds_dma16((r < M && kk < L) ? (const void*)(A + (size_t)r * ldA + kk) : (const void*)zpad,
-                st + XT + 1024 * (4 * j + wave));
+                st + XT + 1024 * (4 * j + li));
     }
   };
   f32x4 acc[MTL][2];
 #pragma unroll
   for (int t = 0; t < MTL; ++t) acc[t][0] = acc[t][1] = zero4();
+  if (loader) {
 #pragma unroll
-  for (int q = 0; q < STG - 1; ++q)
-    if (q < nq) issue(q, q);
+    for (int q = 0; q < STG - 1; ++q)
+      if (q < nq) issue(q, q);
+  }
   const int q4 = lane >> 4, l16 = lane & 15;
   for (int i = 0; i < nq; ++i) {
+    // (waves that issue no loads pass the count at once; all wait for their LDS reads)
     const int later = (nq - 1 - i) < (STG - 2) ? (nq - 1 - i) : (STG - 2);
     wait_oldest_stage<LDPS, STG - 2>(later);
     bare_barrier();  // stage i has landed for every wave; the slot refilled next is free
-    if (i + STG - 1 < nq) issue(i + STG - 1, (i + STG - 1) % STG);
+    if (loader && i + STG - 1 < nq) issue(i + STG - 1, (i + STG - 1) % STG);
+    if (!computer) continue;
     const unsigned char* st = ring[i % STG];
     const unsigned char* ta = st + XT;
 #pragma unroll
@@ -229,6 +243,7 @@ __global__ __launch_bounds__(256) void proj_lds_kernel(const bf16* __restrict__ 
   }
   // lane: row m = 16 t + l16, columns n .. n + 7: the first four from half q4 % 2 of the
   // wave's column pair, the last four from the other half
+  if (!computer) return;
   const int Mb = M - M0;
   const int n = n0 + 32 * wave + 8 * q4;
   if (n >= C) return;
@@ -252,7 +267,8 @@ template <int MTL>
 static hipError_t proj_lds_mt(const void* A, int ldA, int M, int M0, const void* X, int B, int L, int C, void* out0,
                               void* out1, const void* zpad, hipStream_t st) {
   constexpr int MA = (16 * MTL + 31) / 32 * 32;
-  hipLaunchKernelGGL((proj_lds_kernel<MTL, MA, PROJ_STAGES>), dim3((C + 127) / 128, B), dim3(256), 0, st,
+  constexpr int NLD = MTL >= 2 ? 4 : 0;
+  hipLaunchKernelGGL((proj_lds_kernel<MTL, MA, PROJ_STAGES, NLD>), dim3((C + 127) / 128, B), dim3(64 * (4 + NLD)), 0, st,
                      (const bf16*)A, ldA, M, M0, (const bf16*)X, L, C, (bf16*)out0, (bf16*)out1, (const bf16*)zpad);
   return hipGetLastError();
 }
