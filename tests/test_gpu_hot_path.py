@@ -80,6 +80,9 @@ RAGGED = [
     # w (1544 x 11008, 34 MB) too large for L2: g_hat_x reads it once over K slices, with a
     # partial last column strip and a row count (3 * 23) that fills no whole tile
     ("bf16", 3, 70, 1544, 11008, 19, 23),
+    # the same w with 7 * 23 = 161 rows of Q g_y (the middle row-group size of that kernel) and
+    # a token count that leaves a partial last stage of P g_y
+    ("bf16", 7, 40, 1544, 11008, 19, 23),
     # LDS-tiled g_w with K split in two slices (K = 960) and ragged M (1800) and N (1000)
     ("bf16", 32, 40, 1000, 1800, 30, 30),
     # LDS-tiled g_hat_x (270 tiles) with ragged M (40 * 29), N (3400) and a partial last stage
