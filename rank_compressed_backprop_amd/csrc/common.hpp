@@ -30,6 +30,13 @@ constexpr int WAVE = 64;
 // to them in turn by workgroup id
 constexpr int XCDS = 8;
 
+// The work unit of workgroup `id` out of `n` such that each XCD takes a contiguous run of units
+// (ids past the last full round of XCDS workgroups keep their own number).
+__device__ inline int xcd_unit(int id, int n) {
+  const int per = n / XCDS;
+  return id < per * XCDS ? (id % XCDS) * per + id / XCDS : id;
+}
+
 template <class T> struct MM;
 
 template <> struct MM<bf16> {

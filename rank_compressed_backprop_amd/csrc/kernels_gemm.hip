@@ -63,9 +63,7 @@ __global__ __launch_bounds__(64 * (4 + NLD)) void gemm_tiled_kernel(const bf16* 
   const int ntile_all = mtiles * ntiles;
   // XCD-aware order: the tiles of one XCD are a contiguous run, m fastest, so they share
   // the B panel (and neighbouring A panels) in that XCD's L2
-  const int id = blockIdx.x;
-  const int per = ntile_all / XCDS;
-  const int t = id < per * XCDS ? (id % XCDS) * per + id / XCDS : id;
+  const int t = xcd_unit(blockIdx.x, ntile_all);
   const int m0 = (t % mtiles) * GT, n0 = (t / mtiles) * GT;
   const int z = blockIdx.z, S = gridDim.z;
   const int nst = (K + GBK - 1) / GBK;
