@@ -174,8 +174,12 @@ __global__ __launch_bounds__(512) void gemm_ws_kernel(const bf16* __restrict__ A
   constexpr int STAGE = 1024 * (8 + NT);  // bytes: B chunks [g][lane], then A tiles [t][lane]
   __shared__ __attribute__((aligned(1024))) unsigned char ring[STG][STAGE];
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
-  const int z = blockIdx.y, S = gridDim.y;
-  const int col = blockIdx.x * 128 + 8 * (lane & 15);
+  // units slice-major, a contiguous run per XCD: with eight slices each XCD reads one K slice of
+  // A, which then stays in its L2 for every strip
+  const int strips = gridDim.x, S = gridDim.y;
+  const int u = xcd_unit(blockIdx.x + strips * blockIdx.y, strips * S);
+  const int z = u / strips;
+  const int col = (u % strips) * 128 + 8 * (lane & 15);
   const bool col_ok = col < N;
   const int kl = 8 * (lane >> 4);
   const int nsteps = K / mm::KSTEP;
@@ -265,7 +269,12 @@ __global__ __launch_bounds__(768) void gemm_ws2_kernel(const bf16* __restrict__ 
   const int li = wave - 8;
   const int ch = wave & 1, rg = wave >> 1;
   const int MT = (M + 15) / 16;
-  const int n0 = blockIdx.x * 128, z = blockIdx.y, S = gridDim.y;
+  // units slice-major, a contiguous run per XCD: with eight slices each XCD reads one K slice of
+  // A (750 KB at the LLM MLP size), which then stays in its L2 for every strip; in strip order
+  // each XCD would need all of A (6 MB, beyond its 4 MB L2) at every stage
+  const int strips = gridDim.x, S = gridDim.y;
+  const int u = xcd_unit(blockIdx.x + strips * blockIdx.y, strips * S);
+  const int n0 = (u % strips) * 128, z = u / strips;
   const int nst = (K + 63) / 64;
   const int sb = (int)((long)nst * z / S), se = (int)((long)nst * (z + 1) / S), nq = se - sb;
   auto issue = [&](int s, int slot) {
