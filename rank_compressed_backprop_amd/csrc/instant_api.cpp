@@ -474,9 +474,18 @@ instant_status run_backward(instant_layer* h, const void* xhat, const void* gy, 
                                   zpad, st)
               : launch_gemm(h->bf16, true, sc.Pgy, Cy, 0, xhat, Cx, 0, gw, Cx, 0, 1, Cy, Cx, B * Rx, st);
     // g_hat_x = (Q gy) w: M = B * Ry, N = Cx, K = Cy; a w too large for L2 is read once over
-    // K slices, otherwise LDS-staged tiles or register-blocked as for g_w
+    // K slices, whose float32 partials the expansion adds itself; otherwise LDS-staged tiles
+    // or register-blocked as for g_w
+    const int ws = h->bf16 ? gemm_ws_slices(true, false, B * Ry, Cx, Cy) : 0;
+    if (ws && (size_t)ws * B * Ry * Cx <= sc.gpart_floats) {
+      // g_x_b = Q^T g_hat_x_b with g_hat_x summed from its slices inside the expansion
+      if (e == hipSuccess)
+        e = launch_gemm_ws_parts(sc.Qgy, Cy, w, Cx, sc.gpart, sc.gpart_floats, B * Ry, Cx, Cy, zpad, st);
+      if (e == hipSuccess) e = launch_expand_parts(h->Qt(a), LD_QT, sc.gpart, ws, B, Ry, L, Cx, gx, st);
+      return hip_ok(e);
+    }
     if (e == hipSuccess) {
-      if (h->bf16 && !gemm_ws_slices(true, false, B * Ry, Cx, Cy) && gemm_tiled_applies(false, B * Ry, Cx, Cy))
+      if (h->bf16 && !ws && gemm_tiled_applies(false, B * Ry, Cx, Cy))
         e = launch_gemm_tiled(false, sc.Qgy, Cy, w, Cx, sc.gxh, Cx, B * Ry, Cx, Cy, sc.gpart, sc.gpart_floats, zpad,
                               st);
       else

@@ -446,6 +446,98 @@ __global__ __launch_bounds__(NW * WAVE) void expand_kernel(const T* __restrict__
   }
 }
 
+// The expansion with the split-K reduction of g_hat_x folded in (bf16): g_hat_x arrives as the
+// S float32 slices [S][B * R][C] of gemm_ws_kernel / gemm_ws2_kernel. Block (128-column strip,
+// sample, token group): its threads first add the S slices of the sample's R x 128 strip in
+// slice order, rounded to bf16 as splitk_reduce_kernel would (so the result is the same bit for
+// bit), into an LDS operand whose rows R .. KS * KSTEP - 1 are zero; then every wave sweeps its
+// 16-token tiles as expand_kernel does, the B operand read from LDS. This saves the reduction's
+// launch and the round trip of g_hat_x. Grid: (ceil(C / 128), B, TG); S <= 16, C % 8 == 0.
+template <int KS, int NW>
+__global__ __launch_bounds__(NW * WAVE) void expand_parts_kernel(const bf16* __restrict__ At, int ldA,
+                                                                const float* __restrict__ part, int S, int R,
+                                                                int L, int C, bf16* __restrict__ out) {
+  typedef MM<bf16> mm;
+  typedef mm::frag frag;
+  constexpr int KR = KS * mm::KSTEP;  // rows of the LDS operand
+  __shared__ __attribute__((aligned(16))) bf16 gs[KR][128];
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int b = blockIdx.y, c0 = blockIdx.x * 128;
+  const size_t slice = (size_t)gridDim.y * R * C;  // one slice: B * R rows of C
+  // (a thread's slices loaded at once, added in slice order; holding the loads of several
+  // elements at once took registers the sweep below needed: slower on gfx950)
+  for (int e = threadIdx.x; e < KR * 32; e += NW * WAVE) {
+    const int r = e >> 5, c = 4 * (e & 31);
+    float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (r < R && c0 + c < C) {
+      const float* p = part + ((size_t)b * R + r) * C + c0 + c;
+      f32x4 v[16];
+#pragma unroll
+      for (int z = 0; z < 16; ++z)
+        if (z < S) v[z] = *reinterpret_cast<const f32x4*>(p + z * slice);
+      f32x4 acc = v[0];
+#pragma unroll
+      for (int z = 1; z < 16; ++z)
+        if (z < S) {
+          acc[0] += v[z][0];
+          acc[1] += v[z][1];
+          acc[2] += v[z][2];
+          acc[3] += v[z][3];
+        }
+      o[0] = acc[0];
+      o[1] = acc[1];
+      o[2] = acc[2];
+      o[3] = acc[3];
+    }
+    store_row<bf16, 4>(&gs[r][c], o);
+  }
+  __syncthreads();
+
+  const int col = c0 + 8 * (lane & 15);
+  const bool col_ok = col < C;
+  const int kl = mm::G * (lane >> 4);
+  frag bf[KS][8];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) load_strip_T<bf16, 8>(&gs[0][0], 128, ks * mm::KSTEP + kl, KR, 8 * (lane & 15), true, bf[ks]);
+  constexpr int MPW = 4;
+  const int ntl = (L + 15) / 16, step = NW * gridDim.z;
+  for (int tl0 = blockIdx.z * NW + wave; tl0 < ntl; tl0 += step * MPW) {
+    frag af[MPW][KS];
+#pragma unroll
+    for (int i = 0; i < MPW; ++i) {
+      const int tl = tl0 + i * step;
+      const int la = 16 * tl + (lane & 15);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        af[i][ks] = load_frag<bf16>(At + (size_t)la * ldA + ks * mm::KSTEP + kl, tl < ntl && la < L);
+    }
+#pragma unroll
+    for (int i = 0; i < MPW; ++i) {
+      const int tl = tl0 + i * step;
+      if (tl >= ntl) break;
+      f32x4 acc[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = mm::mma(af[i][ks], bf[ks][j], acc[j]);
+      if (col_ok) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int l = 16 * tl + 4 * (lane >> 4) + v;
+          if (l < L) {
+            float o[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] = acc[j][v];
+            store_row_nt<bf16, 8>(out + ((size_t)b * L + l) * C + col, o);
+          }
+        }
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------- fused g_x
 // For layers whose weight stays resident in L2: block (strip, sample group) first forms
 // g_hat_x_b[:, strip] = Qgy_b (Ry x Cy) . w[:, strip] (Cy x 16*SW) on the matrix cores for
@@ -646,6 +738,30 @@ int gemm_ws_slices(bool bf16_io, bool a_trans, int M, int N, int K) {
   return S >= 2 ? S : 0;
 }
 
+// The slices of the read-w-once GEMM (S = gemm_ws_slices(...) > 0): part[z][m][n].
+static hipError_t ws_slices_launch(const void* A, int lda, const void* Bm, int ldb, float* part, int S, int M, int N,
+                                   int K, const void* zpad, hipStream_t st) {
+  const unsigned strips = (unsigned)((N + 127) / 128);
+#define WS2(RT, MA)                                                                                                  \
+  hipLaunchKernelGGL((gemm_ws2_kernel<RT, MA, GWS_STAGES>), dim3(strips, S), dim3(768), 0, st, (const bf16*)A, lda, \
+                     (const bf16*)Bm, ldb, part, M, N, K, (const bf16*)zpad)
+  if (M <= 128) WS2(2, 128);
+  else if (M <= 192) WS2(3, 192);
+  else if (M <= 288) WS2(5, 288);
+  else
+    hipLaunchKernelGGL((gemm_ws_kernel<WS_TPW, 3>), dim3(strips, S), dim3(512), 0, st, (const bf16*)A, lda,
+                       (const bf16*)Bm, ldb, part, M, N, K, (const bf16*)zpad);
+#undef WS2
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_ws_parts(const void* A, int lda, const void* Bm, int ldb, float* part, size_t part_floats,
+                                int M, int N, int K, const void* zpad, hipStream_t st) {
+  const int S = gemm_ws_slices(true, false, M, N, K);
+  if (!S || !part || !zpad || (size_t)S * M * N > part_floats) return hipErrorInvalidValue;
+  return ws_slices_launch(A, lda, Bm, ldb, part, S, M, N, K, zpad, st);
+}
+
 template <class T, bool AT>
 static hipError_t gemm_t(const void* A, int lda, size_t sA, const void* Bm, int ldb, size_t sB, void* Cm, int ldc,
                          size_t sC, int batch, int M, int N, int K, float* part, size_t part_floats,
@@ -658,17 +774,7 @@ static hipError_t gemm_t(const void* A, int lda, size_t sA, const void* Bm, int 
     // 272 x 4096 x 11008: 55.5 us against 71.7 us for row blocks that each stream w again)
     const int S = (part && zpad && batch == 1) ? gemm_ws_slices(true, false, M, N, K) : 0;
     if (S && (size_t)S * M * N <= part_floats) {
-#define WS2(RT, MA)                                                                                                  \
-  hipLaunchKernelGGL((gemm_ws2_kernel<RT, MA, GWS_STAGES>), dim3((unsigned)strips, S), dim3(768), 0, st, (const bf16*)A, \
-                     lda, (const bf16*)Bm, ldb, part, M, N, K, (const bf16*)zpad)
-      if (M <= 128) WS2(2, 128);
-      else if (M <= 192) WS2(3, 192);
-      else if (M <= 288) WS2(5, 288);
-      else
-        hipLaunchKernelGGL((gemm_ws_kernel<WS_TPW, 3>), dim3((unsigned)strips, S), dim3(512), 0, st, (const bf16*)A,
-                           lda, (const bf16*)Bm, ldb, part, M, N, K, (const bf16*)zpad);
-#undef WS2
-      hipError_t e = hipGetLastError();
+      hipError_t e = ws_slices_launch(A, lda, Bm, ldb, part, S, M, N, K, zpad, st);
       if (e != hipSuccess) return e;
       const size_t n4 = (size_t)M * (N / 4);
       hipLaunchKernelGGL(splitk_reduce_kernel<T>, dim3((unsigned)std::min<size_t>((n4 + 255) / 256, 2048)), dim3(256),
@@ -752,6 +858,22 @@ hipError_t launch_expand(bool bf16_io, const void* At, int ldA, const void* Bz, 
                          void* out, hipStream_t st) {
   return bf16_io ? expand_t<bf16>(At, ldA, Bz, B, R, L, C, out, st)
                  : expand_t<float>(At, ldA, Bz, B, R, L, C, out, st);
+}
+
+hipError_t launch_expand_parts(const void* At, int ldA, const float* part, int S, int B, int R, int L, int C, void* out,
+                               hipStream_t st) {
+  if (S < 1 || S > 16 || R < 1 || R > 64 || C % 8 || ldA < 64) return hipErrorInvalidValue;
+  // one block a (strip, sample) over every token, eight waves (measured on gfx950 at the LLM MLP
+  // size, B = 8, L = 2048, C = 4096, R = 34, 8 slices: 34.2 us against 37.3 us for the slices'
+  // reduction and expand_kernel; two token groups 35.3-42.3 us, four waves 34.7-38.5 us)
+  const dim3 grid((C + 127) / 128, B, 1);
+  if (R <= 32)
+    hipLaunchKernelGGL((expand_parts_kernel<1, 8>), grid, dim3(512), 0, st, (const bf16*)At, ldA, part, S, R, L, C,
+                       (bf16*)out);
+  else
+    hipLaunchKernelGGL((expand_parts_kernel<2, 8>), grid, dim3(512), 0, st, (const bf16*)At, ldA, part, S, R, L, C,
+                       (bf16*)out);
+  return hipGetLastError();
 }
 
 template <class T, int MTA, int KS, int SW, int SPB>

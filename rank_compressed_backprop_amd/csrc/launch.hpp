@@ -25,6 +25,10 @@ hipError_t launch_gemm(bool bf16_io, bool a_trans, const void* A, int lda, size_
                        float* part = nullptr, size_t part_floats = 0, const void* zpad = nullptr);
 // K slices (0: not used) of that path for these shapes; it needs S * M * N floats of part.
 int gemm_ws_slices(bool bf16_io, bool a_trans, int M, int N, int K);
+// That path's slices alone (bf16, A [M][lda]): part[z][m][n] for the S = gemm_ws_slices(true,
+// false, M, N, K) > 0 slices, left for launch_expand_parts to add; needs S * M * N floats.
+hipError_t launch_gemm_ws_parts(const void* A, int lda, const void* Bm, int ldb, float* part, size_t part_floats,
+                                int M, int N, int K, const void* zpad, hipStream_t st);
 
 // bf16 C[M][N] = sum_k A(m,k) B[k][n] on LDS-staged 128 x 128 tiles (kernels_gemm.hip).
 // a_kmajor: A stored [K][lda] (m contiguous), else [M][lda]; B stored [K][ldb]. N % 8 == 0,
@@ -41,6 +45,11 @@ hipError_t launch_gemm_tiled(bool a_kmajor, const void* A, int lda, const void* 
 // Out[b][l][c] = sum_{r<R} At[l][r] Bz[b][r][c]; At: [L][ldA], zero beyond column R.
 hipError_t launch_expand(bool bf16_io, const void* At, int ldA, const void* Bz, int B, int R, int L, int C,
                          void* out, hipStream_t st);
+// The same (bf16) with Bz given as the S float32 slices part[z][b * R + r][c] of
+// launch_gemm_ws_parts, added in slice order and rounded as the slices' reduction would round
+// them (identical output). 1 <= S <= 16, R <= 64, C % 8 == 0, ldA >= 64.
+hipError_t launch_expand_parts(const void* At, int ldA, const float* part, int S, int B, int R, int L, int C, void* out,
+                               hipStream_t st);
 
 // gx[b][l][c] = sum_r At[l][r] (sum_k Qgy[b][r][k] w[k][c]) with g_hat_x kept in LDS
 // (rounded to the I/O dtype), and g_w = sum_b Pgy_b^T xhat_b (Pgy [Kw][Cy], xhat [Kw][Cx],
