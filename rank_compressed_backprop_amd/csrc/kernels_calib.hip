@@ -169,6 +169,169 @@ __global__ __launch_bounds__(64 * (4 + NLD)) void syrk_kernel(SyrkSide s0, SyrkS
       *reinterpret_cast<f32x4*>(out + (((wave * 16 + t * 4 + u) * WAVE + lane) * 4)) = acc[t][u];
 }
 
+// ---------------------------------------------------------------- SYRK, wide blocks
+// The same sums for long token axes (bf16): a block owns a 256 x 128 pair of upper-triangle
+// tiles, the 128-row tiles 2I and 2I + 1 against the 128-column tile J >= 2I, over one slice.
+// Each of its four compute waves owns 128 x 64 (eight row tiles of 16 against four column
+// tiles), so a k-step reads 12 fragments for 32 products instead of 8 for 16: a third less
+// LDS traffic per product than the 128 x 128 blocks, whose compute units are bound by their
+// LDS port. A stage holds 64 channels of the 256-row panel (32 KB) and of the 128-row panel
+// (16 KB; none when tile J is one of the pair, which the first panel then holds); four loader
+// waves stream a SYRK_WIDE_STAGES-deep ring. The waves write the float32 partials of each of
+// their two 128 x 128 tiles in the fragment order of syrk_kernel, so syrk_reduce_kernel adds
+// them unchanged, and the sums are the same bit for bit. Below the diagonal (tile 2I + 1
+// against J = 2I) and beyond the last tile nothing is written.
+constexpr int SYRK_WIDE_STAGES = 3;  // 144 KB of LDS: one block a compute unit
+// Token axes of 16 128-row tiles (L > 1920) take the wide blocks (measured on gfx950, SYRK and
+// fold a batch, bit-identical sums: LLM MLP, B = 8, L = 2048, C = 4096 / 11008, 790-803 ->
+// 702-717 us; C = 4096 / 4096, 440-443 -> 397-406 us; at L = 1024 the 128 x 128 blocks, two a
+// compute unit, stay ahead: 50.3 against 51.9 us)
+constexpr int WIDE_MIN_TILES = 16;
+
+int syrk_wide_pairs(int L) {
+  const int T = (L + ST - 1) / ST, m = T / 2;
+  return T % 2 ? (m + 1) * (m + 1) : m * (m + 1);
+}
+
+// sum over I < ceil(T / 2) of T - 2I: m (m + 1) for T = 2m, (m + 1)^2 for T = 2m + 1
+__device__ inline int syrk_wide_pairs_dev(int T) {
+  const int m = T / 2;
+  return T % 2 ? (m + 1) * (m + 1) : m * (m + 1);
+}
+
+__device__ inline void wide_pair(int idx, int T, int& I, int& J) {
+  I = 0;
+  while (idx >= T - 2 * I) {
+    idx -= T - 2 * I;
+    ++I;
+  }
+  J = 2 * I + idx;
+}
+
+__device__ inline int upper_index(int ti, int tj, int T) { return ti * T - ti * (ti - 1) / 2 + (tj - ti); }
+
+template <int STAGES>
+__global__ __launch_bounds__(512) void syrk_wide_kernel(SyrkSide s0, SyrkSide s1, int B, int L,
+                                                        const bf16* __restrict__ zpad) {
+  typedef MM<bf16> mm;
+  typedef mm::frag frag;
+  constexpr int PA = 2 * WPANEL;  // 256-row panel of a stage
+  static_assert(12 * (STAGES - 2) <= 63, "outstanding loads must fit the vmcnt counter");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES][PA + WPANEL];
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int T = (L + ST - 1) / ST;
+  const int ntiles = T * (T + 1) / 2;
+  const int npairs = syrk_wide_pairs_dev(T);
+  int lin = blockIdx.x;
+  const bool second = lin >= npairs * s0.nsplit;
+  if (second) lin -= npairs * s0.nsplit;
+  const bf16* __restrict__ X = (const bf16*)(second ? s1.X : s0.X);
+  const int C = second ? s1.C : s0.C;
+  const int nsplit = second ? s1.nsplit : s0.nsplit;
+  float* __restrict__ part = second ? s1.part : s0.part;
+  int pair, s;
+  if (nsplit % 8 == 0) {  // slice s on XCD s % 8, as in syrk_kernel
+    const int xcd = lin % 8, kq = lin / 8;
+    s = xcd + 8 * (kq / npairs);
+    pair = kq % npairs;
+  } else {
+    s = lin / npairs;
+    pair = lin % npairs;
+  }
+  int I, J;
+  wide_pair(pair, T, I, J);
+  const bool shared = J < 2 * I + 2;  // tile J is one of the pair: the 256-row panel holds it
+  const int pairs_c = ((C + mm::KSTEP - 1) / mm::KSTEP + 1) / 2;
+  const int total = B * pairs_c;
+  const int beg = (int)((long)total * s / nsplit);
+  const int end = (int)((long)total * (s + 1) / nsplit);
+  const int nq = end - beg;
+
+  const bool loader = wave >= 4;
+  const int li = wave - 4;
+  // wave-load j moves rows 8j .. 8j+7 of a panel (1 KB): 32 of the first panel, 16 of the second
+  auto issue = [&](int q, int stage) {
+    const int b = q / pairs_c;
+    const int k0 = (q - b * pairs_c) * 2 * mm::KSTEP;
+    const bf16* __restrict__ Xb = X + (size_t)b * L * C;
+    auto one = [&](int base_row, int j, unsigned char* dst) {
+      const int rloc = 8 * j + (lane >> 3);
+      const int chunk = (lane & 7) ^ slot_swz(rloc);
+      const int row = base_row + rloc;
+      const int kk = k0 + chunk * 8;
+      const bf16* src = (row < L && kk < C) ? Xb + (size_t)row * C + kk : zpad;
+      lds_dma16(src, dst + 1024 * j);
+    };
+#pragma unroll
+    for (int h = 0; h < 8; ++h) one(2 * ST * I, 8 * li + h, lds[stage]);
+    if (!shared) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) one(ST * J, 4 * li + h, lds[stage] + PA);
+    }
+  };
+
+  const int wr = wave >> 1, wc = wave & 1;
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[t][u] = zero4();
+
+  if (loader) {
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+      if (st < nq) issue(beg + st, st);
+  }
+  const int g = lane >> 4;
+  for (int i = 0; i < nq; ++i) {
+    // (compute waves issue no loads and pass the count at once; all wait for their LDS reads)
+    const int younger = (nq - 1 - i) < (STAGES - 2) ? (nq - 1 - i) : (STAGES - 2);
+    if (shared) wait_oldest_stage<8, STAGES - 2>(younger);
+    else wait_oldest_stage<12, STAGES - 2>(younger);
+    bare_barrier();
+    if (loader) {
+      if (i + STAGES - 1 < nq) issue(beg + i + STAGES - 1, (i + STAGES - 1) % STAGES);
+      continue;
+    }
+    const unsigned char* pa = lds[i % STAGES];
+    const unsigned char* pb = shared ? pa + WPANEL * (J - 2 * I) : pa + PA;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      frag af[8], bf[4];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int ra = ST * wr + 16 * t + (lane & 15);
+        af[t] = *reinterpret_cast<const frag*>(pa + ra * 128 + 16 * ((4 * h + g) ^ slot_swz(ra)));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int rb = 64 * wc + 16 * u + (lane & 15);
+        bf[u] = *reinterpret_cast<const frag*>(pb + rb * 128 + 16 * ((4 * h + g) ^ slot_swz(rb)));
+      }
+      // every read of the k-step before its products (left to the compiler's order: 4-10% slower)
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[t][u] = mm::mma(af[t], bf[u], acc[t][u]);
+    }
+  }
+
+  if (loader) return;
+  // rows 128 wr .. of the pair: tile ti = 2I + wr against tj = J, upper triangle only
+  const int ti = 2 * I + wr, tj = J;
+  if (ti >= T || tj < ti) return;
+  float* __restrict__ out = part + ((size_t)s * ntiles + upper_index(ti, tj, T)) * (ST * ST);
+#pragma unroll
+  for (int t8 = 0; t8 < 8; ++t8)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ow = 2 * (t8 >> 2) + wc;  // the 64 x 64 quarter of syrk_kernel's fragment order
+      *reinterpret_cast<f32x4*>(out + (((ow * 16 + (t8 & 3) * 4 + u) * WAVE + lane) * 4)) = acc[t8][u];
+    }
+}
+
 // S[i][j] += sum_s part[s][tile] in split order, float64, for the upper-triangle tiles (or
 // S[i][j] = that sum for a statistic's first batch).
 __global__ __launch_bounds__(256) void syrk_reduce_kernel(SyrkSide s0, SyrkSide s1, int ntiles, int L) {
@@ -340,8 +503,12 @@ static hipError_t syrk_t(const SyrkSide* sides, int nsides, int B, int L, const 
   const SyrkSide s0 = sides[0];
   const SyrkSide s1 = nsides > 1 ? sides[1] : SyrkSide{nullptr, 0, 0, nullptr, nullptr, 0};
   const int nt = syrk_tiles(L);
-  hipLaunchKernelGGL((syrk_kernel<T, SYRK_STAGES, SYRK_LOADERS>), dim3(nt * (s0.nsplit + s1.nsplit)),
-                     dim3(64 * (4 + SYRK_LOADERS)), 0, st, s0, s1, B, L, (const T*)zpad);
+  if (sizeof(T) == 2 && (L + ST - 1) / ST >= WIDE_MIN_TILES)
+    hipLaunchKernelGGL((syrk_wide_kernel<SYRK_WIDE_STAGES>), dim3(syrk_wide_pairs(L) * (s0.nsplit + s1.nsplit)),
+                       dim3(512), 0, st, s0, s1, B, L, (const bf16*)zpad);
+  else
+    hipLaunchKernelGGL((syrk_kernel<T, SYRK_STAGES, SYRK_LOADERS>), dim3(nt * (s0.nsplit + s1.nsplit)),
+                       dim3(64 * (4 + SYRK_LOADERS)), 0, st, s0, s1, B, L, (const T*)zpad);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid(nt, ST * ST / 256, nsides);  // 64 blocks of 256 elements per tile and statistic

@@ -173,6 +173,43 @@ def test_eps_one_keeps_every_direction():
           + check_close("gx", from_dev(gx, "fp32"), ex["gx"], "fp32", mag["gx"]), flush=True)
 
 
+def test_statistics_long_ragged_token_axis():
+    """Statistics (关键设计 1: S = sum over samples of x_b x_b^T, accumulated over batches) on a
+    long ragged token axis, L = 2000 (16 tiles of 128 rows, the last one partly padded), with
+    channel counts that are not multiples of a stage (136, 264), over two batches (the second
+    adds to the first): the float64 means against the oracle's, entry by entry. At this length
+    the SYRK runs in 256 x 128 blocks."""
+    import rank_compressed_backprop_amd as rcb
+    from gpu_util import rel, to_dev
+    rng = np.random.default_rng(33)
+    B, L, Cx, Cy = 3, 2000, 136, 264
+    lay = rcb.InstantLayer(rcb.make_config(L, Cx, Cy, B, R_max=64, p=0, eps=0.9, dtype="bf16"))
+    acc = {"C_X": O.Accumulator(L), "C_G": O.Accumulator(L)}
+    mag = {"C_X": O.Accumulator(L), "C_G": O.Accumulator(L)}
+    for t in range(2):
+        x = W.to_io(rng.standard_normal((B, L, Cx)), "bf16")
+        gy = W.to_io(rng.standard_normal((B, L, Cy)), "bf16")
+        for k, v in (("C_X", x), ("C_G", gy)):
+            v64 = W.io_to_f64(v, "bf16")
+            acc[k].add(v64)
+            mag[k].add(np.abs(v64))
+        assert lay.calibrate(to_dev(x, "bf16"), to_dev(gy, "bf16"), B, finalize=False) == rcb.INSTANT_OK
+    CX = torch.empty((L, L), dtype=torch.float64, device="cuda")
+    CG = torch.empty((L, L), dtype=torch.float64, device="cuda")
+    lay.get_statistics(CX, CG)
+    torch.cuda.synchronize()
+    for name, got in (("C_X", CX.cpu().numpy()), ("C_G", CG.cpu().numpy())):
+        ref, m = acc[name].mean(), mag[name].mean()
+        # bf16 products are exact in float32; a float32 partial sums at most B * 2 * C of them,
+        # whose rounding error is at most that count times 2^-24 times the sum of |terms| (m),
+        # before the float64 sums
+        bound = 2.0 ** -24 * B * 2 * (Cy if name == "C_G" else Cx) * m
+        worst = float(np.max(np.abs(got - ref) - bound))
+        print(f"[stats L={L}] {name}: rel err {rel(got, ref):.2e}, max |err| - bound {worst:.2e}", flush=True)
+        assert np.array_equal(got, got.T), name
+        assert rel(got, ref) < 1e-5 and worst <= 0.0, name
+
+
 def _fresh_layer(dtype="fp32", L=32, C=16, B=2, **kw):
     import rank_compressed_backprop_amd as rcb
     return rcb.InstantLayer(rcb.make_config(L, C, C, B, dtype=dtype, **kw))
