@@ -14,7 +14,7 @@ after 20 untimed ones, each call on its own resident batch (g_y, x_hat, g_x rota
 the resident set, beyond the 256 MB last-level cache); p10 and p90 of the per-call time
 are reported beside it, and the same runs replayed from a HIP graph for comparison.
 
-The driver's `--steps K --warmup W` steps are whole passes of the path on the notes'
+The `--steps K --warmup W` steps are whole passes of the path on the notes'
 schedule (section 整体框架): every step compresses x (x_hat = P x) and runs the low-rank
 backward; the first N_cal steps of every N_t-step window also accumulate the statistics,
 and the last of them finalizes (eigen-decomposition, truncation, new P and Q). Their wall
@@ -70,7 +70,7 @@ def measured_traffic(workload):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100, help="timed steps of the whole path (the driver's K)")
+    ap.add_argument("--steps", type=int, default=100, help="timed steps of the whole path (K)")
     ap.add_argument("--warmup", type=int, default=20, help="untimed steps before them")
     ap.add_argument("--workload", default="bert_attn",
                     help="bert_attn (the headline line); bert_block (every linear layer of a BERT-base "
@@ -224,7 +224,7 @@ def main():
                 raise RuntimeError("calibration failed: " + rcb.instant_status_str(s))
 
     side_st.wait_stream(main_st)  # the resident batches and the set-up's projections
-    # ---- the driver's steps: W untimed, then exactly K timed passes of the whole path
+    # ---- the --steps / --warmup passes: W untimed, then exactly K timed passes of the whole path
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
