@@ -865,7 +865,7 @@ hipError_t launch_expand_parts(const void* At, int ldA, const float* part, int S
   if (S < 1 || S > 16 || R < 1 || R > 64 || C % 8 || ldA < 64) return hipErrorInvalidValue;
   // one block a (strip, sample) over every token, eight waves (measured on gfx950 at the LLM MLP
   // size, B = 8, L = 2048, C = 4096, R = 34, 8 slices: 34.2 us against 37.3 us for the slices'
-  // reduction and expand_kernel; two token groups 35.3-42.3 us, four waves 34.7-38.5 us)
+  // reduction and expand_kernel; two token groups 35.3-41.0 us, four waves 34.7 us)
   const dim3 grid((C + 127) / 128, B, 1);
   if (R <= 32)
     hipLaunchKernelGGL((expand_parts_kernel<1, 8>), grid, dim3(512), 0, st, (const bf16*)At, ldA, part, S, R, L, C,
